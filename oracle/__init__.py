@@ -1,0 +1,8 @@
+"""fp64 CPU oracle of the fused clip + AdamW optimizer step.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, the smoke check and the
+benchmark's CPU-baseline leg, never by the product library or its binding.
+"""
+from .adamw_fp64 import (CLIP_EPS, Group, Oracle, StepStats, adamw_update,  # noqa: F401
+                         clip_coefficient, global_norm, normalized_sumsq,
+                         update_elements, widen_grad)

@@ -1,0 +1,125 @@
+"""Shapes and schedules of the synthetic workloads (no optimizer arithmetic here)."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from tensor_optimizer_step_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_constants.json")
+
+
+def test_page_constants():
+    c = json.load(open(GOLDEN))
+    assert W.PAGE_LR == c["actor_lr"]
+    assert W.PAGE_MAX_NORM == c["grad_clip_max_norm"]
+    assert c["ppo_mini_batch_size"] // c["ppo_micro_batch_size"] == c["num_micro_batches"]
+    ae = W.action_expert()
+    assert all(g.lr == c["actor_lr"] for g in ae.groups)
+    assert ae.max_norm == c["grad_clip_max_norm"]
+
+
+def test_tiny():
+    wl = W.tiny()
+    assert wl.n_tensors == 64
+    sizes = [t.numel for t in wl.tensors]
+    assert min(sizes) >= 1 and max(sizes) <= 65536
+    assert wl.grad_divisor == 4.0 and wl.steps == 1
+    assert wl.trainable_numel == sum(sizes)
+
+
+def test_action_expert_shape():
+    wl = W.action_expert()
+    assert wl.n_tensors == 164
+    assert wl.trainable_numel == 302_092_288
+    assert sum(1 for t in wl.tensors if t.group == 1) == 36
+    assert all(t.grad_dtype == W.BF16 for t in wl.tensors)
+    assert [g.weight_decay for g in wl.groups] == [0.01, 0.0]
+
+
+def test_launch_bound_shape():
+    wl = W.launch_bound()
+    assert wl.n_tensors == 20000
+    frozen = [t for t in wl.tensors if not t.trainable]
+    assert len(frozen) == 6000
+    sizes = np.array([t.numel for t in wl.tensors])
+    assert sizes.min() >= 1 and sizes.max() <= 4096
+    assert abs(wl.total_numel - 20000 * 2048.5) < 0.02 * wl.total_numel
+    lrs = [wl.lrs_for_step(k) for k in range(1, 11)]
+    assert lrs[-1] == [g.lr for g in wl.groups]
+    assert lrs[0][0] == pytest.approx(wl.groups[0].lr / 10)
+
+
+def test_backbone_7b_shape():
+    wl = W.backbone_7b()
+    assert wl.n_tensors == 291
+    assert wl.trainable_numel == 6_738_939_904
+    # global norm alternates between 0.5x and 5x max_norm in expectation
+    n = wl.trainable_numel
+    assert wl.grad_std(1) * math.sqrt(n) == pytest.approx(0.5)
+    assert wl.grad_std(2) * math.sqrt(n) == pytest.approx(5.0)
+
+
+def test_sharded_7b_layout():
+    lay = W.sharded_7b()
+    base = lay.base
+    assert lay.n_descriptors == 488
+    per = 1_684_668_416
+    norm_numel = 65 * 4096
+    assert lay.shard_numel == [per + norm_numel] * 4
+    mats = [p for p in lay.pieces if base.tensors[p.tensor].group == 0]
+    reps = [p for p in lay.pieces if base.tensors[p.tensor].group == 1]
+    assert len(mats) == 228 and len(reps) == 260
+    # every matrix element appears exactly once, cuts are multiples of 8
+    covered = {}
+    for p in mats:
+        covered.setdefault(p.tensor, []).append((p.t_offset, p.numel))
+        assert p.s_offset % 8 == 0 and p.owner
+    for i, segs in covered.items():
+        segs.sort()
+        off = 0
+        for o, n in segs:
+            assert o == off
+            off += n
+        assert off == base.tensors[i].numel
+    straddling = [i for i, s in covered.items() if len(s) > 1]
+    assert len(straddling) == 2
+    # replicas: owned by shard 0 only, one copy per shard
+    for s in range(4):
+        rs = [p for p in reps if p.shard == s]
+        assert len(rs) == 65 and all(p.owner == (s == 0) for p in rs)
+    assert sum(p.numel for p in lay.pieces if p.owner) == base.trainable_numel
+    # pieces inside a shard do not overlap and fit the allocation
+    for s in range(4):
+        iv = sorted((p.s_offset, p.s_offset + p.numel) for p in lay.pieces if p.shard == s)
+        assert iv[0][0] == 0 and iv[-1][1] == lay.shard_numel[s]
+        assert all(a[1] == b[0] for a, b in zip(iv, iv[1:]))
+
+
+def test_cosine_schedule():
+    lay = W.sharded_7b()
+    lrs = [lay.base.lrs_for_step(k)[0] for k in range(1, 11)]
+    assert lrs[0] == pytest.approx(W.PAGE_LR)
+    assert all(a > b for a, b in zip(lrs, lrs[1:]))
+    assert lrs[-1] > 0
+
+
+def test_values_are_seeded():
+    torch = pytest.importorskip("torch")
+    wl = W.tiny()
+    a = W.param_values(wl, 3)
+    b = W.param_values(wl, 3)
+    assert torch.equal(a, b)
+    g1 = W.grad_values(wl, 3, 1)
+    g2 = W.grad_values(wl, 3, 2)
+    assert not torch.equal(g1, g2)
+    lb = W.launch_bound(n_tensors=50)
+    frozen = [i for i, t in enumerate(lb.tensors) if not t.trainable]
+    assert torch.isnan(W.grad_values(lb, frozen[0], 1)).all()
+    ae = W.action_expert(blocks=1, d=64, mlp=128)
+    g = W.grad_values(ae, 0, 1)
+    assert g.dtype == torch.bfloat16
+    bits = W.to_numpy_grad(g)
+    assert bits.dtype == np.uint16
