@@ -1,0 +1,242 @@
+"""Benchmark of the fused clip + AdamW optimizer step on one MI355X.
+
+One step = the whole hot path over one synthetic batch of gradients: the norm
+pass (owned fp64 sum of squares + on-device clip decision) and the fused
+update pass, replayed from the captured HIP graph.  Inputs are resident in HBM
+before the timed region starts.
+
+Prints ONE JSON line.  ``value`` is trainable param-elements updated per
+second; the line also carries the achieved model GB/s, the roofline of the
+dominant kernel (the update pass, HBM-bound) measured with HIP events on the
+stream it is launched on, and the fp64 CPU oracle timed on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload action_expert]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fused clip+AdamW step: param-elements/s and achieved HBM GB/s (% of peak)"
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
+KERNEL_SRC = os.path.join(ROOT, "tensor_optimizer_step_amd", "csrc", "kernels.hip")
+TRAFFIC_DIR = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="action_expert",
+                    choices=["action_expert", "backbone_7b", "launch_bound", "tiny"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample (0 disables it)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (for HBM counter scaling)")
+    return ap.parse_args()
+
+
+def kernel_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def bytes_per_step(wl) -> dict:
+    """Algorithmic HBM bytes: norm pass reads g once; update pass reads g,p,m,v
+    and writes p,m,v (fp32 state, 2- or 4-byte gradient)."""
+    from tensor_optimizer_step_amd import workloads as W
+    p1 = p2 = 0
+    for t in wl.tensors:
+        if not t.trainable:
+            continue
+        gsz = 2 if t.grad_dtype == W.BF16 else 4
+        p1 += gsz * t.numel
+        p2 += (gsz + 12 + 12) * t.numel
+    return {"pass1": p1, "pass2": p2, "total": p1 + p2}
+
+
+def copy_calibration(torch):
+    """A plain copy of 2 GiB, the counter-scaling reference for FETCH/WRITE_SIZE."""
+    n = 1 << 29
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(10):
+        b.copy_(a)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / 10
+    print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "ms": ms,
+                      "GBps": 8 * n / ms / 1e6}), flush=True)
+
+
+def cpu_baseline(wl, seconds: float) -> dict:
+    """Time the fp64 oracle on the first tensors of the workload (bounded)."""
+    import numpy as np
+    import oracle as O
+    from tensor_optimizer_step_amd import workloads as W
+
+    budget = 20_000_000
+    idx, tot = [], 0
+    for i, t in enumerate(wl.tensors):
+        if not t.trainable:
+            continue
+        if idx and tot + t.numel > budget:
+            break
+        idx.append(i)
+        tot += t.numel
+    p0 = [W.param_values(wl, i).numpy() for i in idx]
+    grads = [W.to_numpy_grad(W.grad_values(wl, i, 1)) for i in idx]
+    ora = O.Oracle(p0, [True] * len(idx), [True] * len(idx), [wl.tensors[i].group for i in idx],
+                   [O.Group(h.lr, h.weight_decay, h.beta1, h.beta2, h.eps) for h in wl.groups],
+                   wl.max_norm, wl.grad_divisor)
+    ora.step(grads)                    # untimed warm-up (page faults)
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < 3 or time.perf_counter() - t_start < seconds:
+        t0 = time.perf_counter()
+        ora.step(grads)
+        times.append(time.perf_counter() - t0)
+    med = sorted(times)[len(times) // 2]
+    return {"value": tot / med, "unit": "param-elements/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {len(idx)} tensors of {wl.name} ({tot} elements), "
+                      f"{len(times)} timed steps, median step {med:.3f} s, NumPy float64, one thread"}
+
+
+def load_traffic(workload: str, algo_bytes: int):
+    """HBM bytes per update-pass launch from committed rocprofv3 counters, if they
+    were taken on the current kernel source; else None."""
+    path = os.path.join(TRAFFIC_DIR, f"traffic_pass2_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_sha256_16") != kernel_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported here "
+              "(the optimizer step shards per rank; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+
+    from tensor_optimizer_step_amd import somaopt
+    from tensor_optimizer_step_amd import workloads as W
+
+    somaopt.load()
+    wl = W.WORKLOADS[args.workload]()
+    dev = "cuda"
+    print(f"[bench] {wl.name}: {wl.n_tensors} tensors, {wl.trainable_numel} trainable elements",
+          file=sys.stderr, flush=True)
+    p, g, m, v = [], [], [], []
+    for i, t in enumerate(wl.tensors):
+        p.append(W.param_values(wl, i, dev))
+        g.append(W.grad_values(wl, i, 1, dev))
+        m.append(torch.zeros(t.numel, device=dev))
+        v.append(torch.zeros(t.numel, device=dev))
+    stream = torch.cuda.current_stream()
+    opt = somaopt.FusedAdamW(p, g, m, v, [t.group for t in wl.tensors], wl.groups, wl.max_norm,
+                             wl.grad_divisor, trainable=[t.trainable for t in wl.tensors],
+                             stream=stream)
+    info = opt.plan_info()
+    opt.capture()
+    bts = bytes_per_step(wl)
+    n_elem = wl.trainable_numel
+
+    # warm-up, then exactly K timed replays of the captured step
+    for k in range(args.warmup):
+        opt.set_lrs(wl.lrs_for_step(1 + k % wl.steps), stream)
+        opt.replay(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    scheduled = wl.schedule != "constant"
+    for k in range(args.steps):
+        if scheduled:
+            opt.set_lrs(wl.lrs_for_step(1 + k % wl.steps), stream)
+        opt.replay(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_s = (t1 - t0) / args.steps
+    print(f"[bench] {args.steps} graph steps: {step_s * 1e3:.4f} ms/step", file=sys.stderr,
+          flush=True)
+
+    # per-kernel durations: eager steps with HIP events on the launch stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for e0, e1, e2 in ev:
+        e0.record(stream)
+        opt.grad_sqnorm(stream)
+        e1.record(stream)
+        opt.fused_adamw_step(stream)
+        e2.record(stream)
+    torch.cuda.synchronize()
+    p1_ms = sum(e0.elapsed_time(e1) for e0, e1, _ in ev) / len(ev)
+    p2_ms = sum(e1.elapsed_time(e2) for _, e1, e2 in ev) / len(ev)
+    stats, steps_done = opt.read_stats()
+    if not all(math.isfinite(x) for x in (stats.norm, stats.clip_coef)):
+        raise RuntimeError("non-finite statistics in the benchmark run")
+
+    p2_gbs = bts["pass2"] / (p2_ms * 1e-3) / 1e9
+    traffic = load_traffic(wl.name, bts["pass2"])
+    roofline = {"bound": "hbm", "achieved": round(p2_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(p2_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "adamw_pass2", "algorithmic_bytes_per_launch": bts["pass2"],
+                "avg_launch_ms": round(p2_ms, 5),
+                "pass1_avg_launch_ms": round(p1_ms, 5),
+                "pass1_GBps": round(bts["pass1"] / (p1_ms * 1e-3) / 1e9, 1)}
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+    model_gbs = bts["total"] / step_s / 1e9
+    out = {
+        "metric": METRIC,
+        "value": n_elem / step_s,
+        "unit": "param-elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "hbm_GBps": round(model_gbs, 1),
+        "hbm_frac_of_peak": round(model_gbs / HBM_PEAK_GBS, 4),
+        "config": {"workload": wl.name, "tensors": wl.n_tensors, "trainable_elements": n_elem,
+                   "grad_dtype": wl.tensors[0].grad_dtype, "state_dtype": "f32",
+                   "model_bytes_per_step": bts["total"], "groups": len(wl.groups),
+                   "pass1_blocks": info.pass1_blocks, "pass2_blocks": info.pass2_blocks,
+                   "graph": True},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    opt.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

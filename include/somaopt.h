@@ -1,0 +1,243 @@
+/*
+ * somaopt.h - fused clip + AdamW optimizer step for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (SomaSpeed landing page, paragraphs "After
+ * backward, each trainable tensor has a gradient ..." and "SomaSpeed batches
+ * that work across tensors ..."): after backward, over a table of many
+ * trainable tensors,
+ *   1. normalize the gradients for the effective batch (divide by D),
+ *   2. measure one global L2 norm in which every owned gradient element counts
+ *      once,
+ *   3. take one global clip decision  c = min(1, max_norm / (norm + 1e-6))
+ *      (the clip_grad_norm_ rule the veRL page applies with max_norm = 1.0,
+ *      section 4.2 "Phase 4: Actor Update"),
+ *   4. in one fused pass that reads the ORIGINAL gradient, apply
+ *      normalization, clipping and decoupled-weight-decay AdamW to the fp32
+ *      weight and both fp32 moments, per parameter group:
+ *        g_hat = g * c / D
+ *        m     = beta1 * m + (1 - beta1) * g_hat
+ *        v     = beta2 * v + (1 - beta2) * g_hat^2
+ *        p     = p - lr*wd*p - (lr / (1 - beta1^t)) * m / (sqrt(v / (1 - beta2^t)) + eps)
+ *      with t the group's update count, 1 on the first update.
+ * Gradient buffers are never written and frozen tensors are never read or
+ * written (same paragraph).  bf16 gradients are widened to fp32 for the update
+ * and the optimizer state stays fp32 (RLinf page, "Retaining Low-Precision
+ * Gradients").
+ *
+ * Conventions for every call:
+ *   - Pointers in somaopt_tensor_desc are DEVICE pointers on the device that
+ *     is current when somaopt_init_tensor_table is called; the caller owns the
+ *     memory, must keep it alive and at the same address for the handle's
+ *     lifetime (no reallocation of gradients between steps).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Step-path calls only enqueue work on it and never wait for the device.
+ *   - Every call returns a somaopt_status; on failure somaopt_last_error()
+ *     returns a message (thread-local, valid until the next call on the same
+ *     thread).  Nothing throws across this interface.
+ *   - A handle is used from one host thread at a time.  Calls that mutate the
+ *     device-side state (set_groups, set_clip, set_step, the step itself) are
+ *     ordered by the stream they are enqueued on; use one stream per handle or
+ *     order streams yourself.
+ */
+#ifndef SOMAOPT_H
+#define SOMAOPT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SOMAOPT_MAX_GROUPS 64
+
+typedef enum {
+    SOMAOPT_OK = 0,
+    SOMAOPT_E_INVALID = -1, /* an argument or a tensor descriptor is invalid      */
+    SOMAOPT_E_HIP = -2,     /* a HIP runtime call or kernel launch failed         */
+    SOMAOPT_E_NOMEM = -3,   /* a device or host allocation failed                 */
+    SOMAOPT_E_STATE = -4    /* call order violated (see each call)                */
+} somaopt_status;
+
+typedef enum {
+    SOMAOPT_F32 = 0,  /* IEEE binary32 gradient                                  */
+    SOMAOPT_BF16 = 1  /* bfloat16 gradient (top 16 bits of a binary32)           */
+} somaopt_dtype;
+
+/* One entry of the tensor table.  A tensor cut by a shard boundary, or a
+ * replica, is simply another entry whose pointers address that piece. */
+typedef struct {
+    void* param;          /* fp32 weights, numel elements, updated in place    */
+    const void* grad;     /* gradient, grad_dtype, numel elements, read only   */
+    void* exp_avg;        /* fp32 first moment m, updated in place             */
+    void* exp_avg_sq;     /* fp32 second moment v, updated in place            */
+    int64_t numel;        /* >= 0; 0 is allowed and skipped                    */
+    int32_t grad_dtype;   /* somaopt_dtype                                      */
+    int32_t group;        /* parameter group, 0 <= group < n_groups             */
+    int32_t trainable;    /* 0: frozen; never read or written, pointers may be NULL */
+    int32_t owner;        /* 1: counts in the global norm; 0: updated only (a
+                             replica or a piece another rank owns)              */
+} somaopt_tensor_desc;
+
+/* Per-group hyperparameters (the group's lr at this step, after the caller's
+ * schedule).  Doubles on input; derived per-step constants are computed on the
+ * device in fp64 and the elementwise update runs in fp32. */
+typedef struct {
+    double lr;
+    double weight_decay;
+    double beta1;
+    double beta2;
+    double eps;
+} somaopt_group;
+
+/* Step statistics, resident in device memory (see somaopt_device_stats). */
+typedef struct {
+    double sumsq;        /* sum over owned trainable elements of g^2 (raw g)  */
+    double norm;         /* sqrt(sumsq) / grad_divisor                        */
+    double clip_coef;    /* min(1, max_norm / (norm + 1e-6)); NaN if norm is NaN */
+    double grad_scale;   /* clip_coef / grad_divisor: multiplies raw g        */
+    int32_t nonfinite;   /* 1 if sumsq is NaN or infinite (step still runs)   */
+    int32_t n_groups;
+} somaopt_stats;
+
+/* Counts describing the device tables built at init. */
+typedef struct {
+    int64_t n_tensors;          /* descriptors passed in                       */
+    int64_t n_trainable;        /* descriptors with trainable != 0             */
+    int64_t trainable_numel;    /* elements updated per step (N)               */
+    int64_t owned_numel;        /* elements summed in the norm (N_o)           */
+    int64_t pass1_segments;     /* gradient segments read by the norm pass     */
+    int64_t pass1_blocks;       /* workgroups of the norm pass                 */
+    int64_t pass2_segments;     /* segments of the update pass                 */
+    int64_t pass2_blocks;       /* workgroups of the update pass               */
+    int64_t scalar_segments;    /* update segments that cannot use 16-byte loads */
+    int64_t pass1_chunk;        /* max elements per norm-pass workgroup        */
+    int64_t pass2_chunk;        /* max elements per update-pass workgroup      */
+    int64_t table_bytes;        /* device bytes of the descriptor tables       */
+} somaopt_plan_info;
+
+/* One row of the host-side plan, for inspection (somaopt_debug_plan). */
+typedef struct {
+    int64_t tensor;      /* descriptor index                                   */
+    int64_t offset;      /* first element of the segment inside the tensor    */
+    int64_t numel;       /* elements in the segment                           */
+    int64_t nvec;        /* aligned vectors after the scalar head             */
+    int32_t head;        /* scalar elements before the first vector           */
+    int32_t tail;        /* scalar elements after the last vector             */
+    int32_t vec_elems;   /* elements per vector (0: all scalar)               */
+    int32_t block;       /* workgroup index that processes the segment        */
+} somaopt_plan_segment;
+
+typedef struct somaopt_handle somaopt_handle;
+
+/*
+ * Build the device-resident tensor and chunk tables (the batching across
+ * tensors of the landing page's "SomaSpeed batches that work across tensors"
+ * paragraph) so that each pass is one kernel launch over all tensors.
+ *
+ *   descs[n_tensors]   tensor table (host memory, copied; may be freed after)
+ *   groups[n_groups]   initial per-group hyperparameters, 1..SOMAOPT_MAX_GROUPS
+ *   max_norm           clip threshold M (> 0)
+ *   grad_divisor       effective-batch divisor D (> 0), e.g. the number of
+ *                      micro-batches accumulated (veRL page, section 4.2)
+ *   initial_step       updates already applied (0 for a fresh optimizer;
+ *                      resume passes the saved count)
+ *   stream             stream for the one-time upload; this call waits for it
+ *   out                receives the new handle
+ *
+ * Frozen descriptors are dropped here and never appear in any table.
+ * Validation (SOMAOPT_E_INVALID): NULL pointer or misaligned (4-byte fp32,
+ * 2-byte bf16) buffer on a trainable tensor, numel < 0, group out of range,
+ * unknown dtype, owner/trainable not 0/1, any overlap between the p, m, v
+ * buffers of trainable tensors or between a gradient and any p/m/v buffer,
+ * a buffer that is not device memory of the current device or that runs past
+ * the end of its allocation (skipped if SOMAOPT_SKIP_POINTER_CHECK=1).
+ * Tuning (optional environment): SOMAOPT_PASS1_CHUNK, SOMAOPT_PASS2_CHUNK =
+ * maximum elements per workgroup of the norm / update pass.
+ */
+int somaopt_init_tensor_table(const somaopt_tensor_desc* descs, int64_t n_tensors,
+                              const somaopt_group* groups, int32_t n_groups,
+                              double max_norm, double grad_divisor, int64_t initial_step,
+                              void* stream, somaopt_handle** out);
+
+/*
+ * Norm pass: one launch over every owned gradient segment, fp64 sum of squares
+ * per workgroup, and (in the last workgroup to finish, on the device, no host
+ * sync) the fixed-order global sum, the norm, the clip coefficient and each
+ * group's bias-corrected constants for the next update (landing page: "It
+ * first computes the statistics needed for one global clipping decision,
+ * accounting for distributed ownership so that each gradient shard
+ * contributes once").
+ * Calling it again before somaopt_fused_adamw_step recomputes the same
+ * statistics for the same pending update (the step count advances once).
+ */
+int somaopt_grad_sqnorm(somaopt_handle* h, void* stream);
+
+/*
+ * Update pass: one launch over every trainable segment; reads g, p, m, v and
+ * writes p, m, v using the statistics the preceding somaopt_grad_sqnorm left
+ * on the device (landing page: "The final update reads the original gradients
+ * and applies normalization, clipping, and AdamW together").
+ * SOMAOPT_E_STATE if no somaopt_grad_sqnorm preceded it since the last update.
+ */
+int somaopt_fused_adamw_step(somaopt_handle* h, void* stream);
+
+/* Replace every group's hyperparameters (n_groups must equal the handle's).
+ * Enqueued as a tiny kernel whose arguments carry the values, so the host
+ * array may be reused at once; a learning-rate schedule calls this before
+ * each step ("learning-rate schedules retain their configured behavior"). */
+int somaopt_set_groups(somaopt_handle* h, const somaopt_group* groups, int32_t n_groups,
+                       void* stream);
+
+/* Replace max_norm and grad_divisor (both > 0), stream ordered. */
+int somaopt_set_clip(somaopt_handle* h, double max_norm, double grad_divisor, void* stream);
+
+/* Set every group's completed-update count (resume), stream ordered.  Clears
+ * a pending norm pass. */
+int somaopt_set_step(somaopt_handle* h, int64_t step, void* stream);
+
+/* Capture {norm pass, update pass} into a HIP graph owned by the handle
+ * (captured on a private stream; nothing runs).  Replaces an earlier graph. */
+int somaopt_capture_step(somaopt_handle* h);
+
+/* Launch the captured step on `stream`: one full step (norm pass with its
+ * step advance, then update pass).  SOMAOPT_E_STATE if not captured or if an
+ * eager norm pass is pending. */
+int somaopt_replay_step(somaopt_handle* h, void* stream);
+
+/* Device address of the somaopt_stats block (valid for the handle's life). */
+int somaopt_device_stats(somaopt_handle* h, const void** stats_dev);
+
+/* Copy the stats and the per-group update counts (steps_out may be NULL,
+ * else n_groups entries) to the host.  Waits for `stream`: not for the step
+ * path. */
+int somaopt_read_stats(somaopt_handle* h, somaopt_stats* out, int64_t* steps_out, void* stream);
+
+/* Counts of the tables built at init. */
+int somaopt_get_plan_info(const somaopt_handle* h, somaopt_plan_info* out);
+
+/*
+ * Host-only: validate `descs` (the checks of init that need no device) and
+ * build the plan of one pass (pass = 1: norm pass, 2: update pass) without
+ * touching a GPU.  Writes up to `cap` rows to `segs` (may be NULL) and the
+ * counts to `info` (may be NULL).  pass1_chunk / pass2_chunk <= 0 select the
+ * defaults.  Returns the number of segments of that pass, or a negative status.
+ */
+int64_t somaopt_debug_plan(const somaopt_tensor_desc* descs, int64_t n_tensors, int32_t n_groups,
+                           int32_t pass, int64_t pass1_chunk, int64_t pass2_chunk,
+                           somaopt_plan_segment* segs, int64_t cap, somaopt_plan_info* info);
+
+/* Release the handle's device tables, graph and private stream.  Waits for
+ * work the handle enqueued.  NULL is ignored. */
+void somaopt_destroy(somaopt_handle* h);
+
+/* Message for the last failed call on this thread ("" if none). */
+const char* somaopt_last_error(void);
+
+/* Library version string. */
+const char* somaopt_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SOMAOPT_H */

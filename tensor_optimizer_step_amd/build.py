@@ -1,0 +1,55 @@
+"""Build ``libsomaopt.so`` (gfx950) in-tree with hipcc.
+
+Usage: ``python -m tensor_optimizer_step_amd.build`` (or ``build()``).  Always
+recompiles.  All HIP code is compiled with packed-fp32 instructions disabled.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libsomaopt.so")
+ARCH = os.environ.get("SOMAOPT_ARCH", "gfx950")
+
+SOURCES = ["plan.cpp", "somaopt.cpp", "kernels.hip"]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libsomaopt.so)")
+
+
+def command(out: str) -> list:
+    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+            "-Wall", "-Wno-unused-function",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-I", INCLUDE, "-I", CSRC,
+            *[os.path.join(CSRC, s) for s in SOURCES], "-o", out]
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB + f".tmp{os.getpid()}"
+    cmd = command(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        if os.path.exists(tmp):
+            os.unlink(tmp)
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}\n{res.stderr}")
+    if verbose and res.stderr.strip():
+        print(res.stderr, file=sys.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,416 @@
+// gfx950 kernels of the fused clip + AdamW optimizer step.
+//
+// Pass 1 (norm pass): every workgroup streams the owned gradient segments of
+// its block with 16-byte loads, squares and accumulates in fp64, reduces across
+// the wavefront with DPP row permutes and across waves through LDS, and stores
+// one partial per workgroup.  The last workgroup to finish (a completion
+// ticket, no spinning) adds the partials in index order, so the global sum is
+// bitwise reproducible, and derives the norm, the clip coefficient and each
+// group's bias-corrected constants on the device.  SomaSpeed landing page,
+// paragraph "SomaSpeed batches that work across tensors ...": statistics for
+// one global clipping decision, each gradient shard counted once.
+//
+// Pass 2 (update pass): a streaming elementwise kernel over every trainable
+// segment that reads g, p, m, v and writes p, m, v in one pass, applying the
+// effective-batch normalization, the clip coefficient and decoupled AdamW
+// together (same paragraph: "The final update reads the original gradients and
+// applies normalization, clipping, and AdamW together").  HBM-bound, so plain
+// fp32 FMA arithmetic, no matrix cores.
+#include <hip/hip_runtime.h>
+
+#include "kernels.hpp"
+
+namespace somaopt {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Address spaces: tensor data is global memory (global_load/store with a
+// scalar base); the descriptor tables and the optimizer state are read through
+// the constant space so that they arrive by scalar loads into SGPRs.
+#define AS_GLOBAL __attribute__((address_space(1)))
+#define AS_CONST __attribute__((address_space(4)))
+
+template <typename T>
+__device__ __forceinline__ AS_GLOBAL T* gptr(const void* p) {
+    return (AS_GLOBAL T*)(p);
+}
+template <typename T>
+__device__ __forceinline__ const AS_CONST T* cptr(const void* p) {
+    return (const AS_CONST T*)(p);
+}
+// Copy a table entry out of the constant space (scalar loads).  The host pass
+// of the single-source compile cannot copy across address spaces and never
+// runs this code, so it only sees a stand-in.
+template <typename T>
+__device__ __forceinline__ T cload(const AS_CONST T* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return *p;
+#else
+    (void)p;
+    return T{};
+#endif
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_one(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// ---------------------------------------------------------------- reductions
+
+// Move a double across lanes with one DPP control (applied to both halves).
+template <int CTRL>
+__device__ __forceinline__ double dpp_double(double x) {
+    int lo = __double2loint(x);
+    int hi = __double2hiint(x);
+    lo = __builtin_amdgcn_update_dpp(0, lo, CTRL, 0xF, 0xF, false);
+    hi = __builtin_amdgcn_update_dpp(0, hi, CTRL, 0xF, 0xF, false);
+    return __hiloint2double(hi, lo);
+}
+
+__device__ __forceinline__ double readlane_double(double x, int lane) {
+    int lo = __builtin_amdgcn_readlane(__double2loint(x), lane);
+    int hi = __builtin_amdgcn_readlane(__double2hiint(x), lane);
+    return __hiloint2double(hi, lo);
+}
+
+// Sum over the 64 lanes of a wavefront, identical in every lane, fixed order.
+// Inside each 16-lane row: swap neighbours (quad_perm 1,0,3,2), swap pairs
+// (quad_perm 2,3,0,1), mirror half-rows, mirror the row; then the four row
+// sums are read from lanes 0, 16, 32, 48 and added as (r0 + r1) + (r2 + r3).
+// Must be called with all 64 lanes active.
+__device__ __forceinline__ double wave_sum(double x) {
+    x += dpp_double<0xB1>(x);    // quad_perm [1,0,3,2]
+    x += dpp_double<0x4E>(x);    // quad_perm [2,3,0,1]
+    x += dpp_double<0x141>(x);   // row_half_mirror
+    x += dpp_double<0x140>(x);   // row_mirror
+    const double r0 = readlane_double(x, 0);
+    const double r1 = readlane_double(x, 16);
+    const double r2 = readlane_double(x, 32);
+    const double r3 = readlane_double(x, 48);
+    return (r0 + r1) + (r2 + r3);
+}
+
+// Workgroup sum (valid in thread 0); waves are added in index order.
+template <int BS>
+__device__ __forceinline__ double block_sum(double x, double* lds) {
+    constexpr int kWaves = BS / 64;
+    const double w = wave_sum(x);
+    if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = w;
+    __syncthreads();
+    double s = 0.0;
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int k = 0; k < kWaves; ++k) s += lds[k];
+    }
+    return s;
+}
+
+// ------------------------------------------------------------------ pass 1
+
+template <int BS>
+__device__ __forceinline__ void segment_sumsq(const Seg1& sg, int tid, double& a0, double& a1) {
+    if (sg.dtype == SOMAOPT_BF16) {
+        const AS_GLOBAL uint16_t* g = gptr<uint16_t>(sg.g);
+        if ((uint32_t)tid < sg.head) {
+            const double x = bf16_one(g[tid]);
+            a0 = fma(x, x, a0);
+        }
+        const AS_GLOBAL u32x4* gv = (const AS_GLOBAL u32x4*)(g + sg.head);
+#pragma unroll 2
+        for (uint32_t i = tid; i < sg.nvec; i += BS) {
+            const u32x4 q = gv[i];
+            double x;
+            x = bf16_lo(q.x); a0 = fma(x, x, a0);
+            x = bf16_hi(q.x); a1 = fma(x, x, a1);
+            x = bf16_lo(q.y); a0 = fma(x, x, a0);
+            x = bf16_hi(q.y); a1 = fma(x, x, a1);
+            x = bf16_lo(q.z); a0 = fma(x, x, a0);
+            x = bf16_hi(q.z); a1 = fma(x, x, a1);
+            x = bf16_lo(q.w); a0 = fma(x, x, a0);
+            x = bf16_hi(q.w); a1 = fma(x, x, a1);
+        }
+        if ((uint32_t)tid < sg.tail) {
+            const double x = bf16_one(g[sg.head + 8 * (size_t)sg.nvec + tid]);
+            a1 = fma(x, x, a1);
+        }
+    } else {
+        const AS_GLOBAL float* g = gptr<float>(sg.g);
+        if ((uint32_t)tid < sg.head) {
+            const double x = g[tid];
+            a0 = fma(x, x, a0);
+        }
+        const AS_GLOBAL f32x4* gv = (const AS_GLOBAL f32x4*)(g + sg.head);
+#pragma unroll 2
+        for (uint32_t i = tid; i < sg.nvec; i += BS) {
+            const f32x4 q = gv[i];
+            double x;
+            x = q.x; a0 = fma(x, x, a0);
+            x = q.y; a1 = fma(x, x, a1);
+            x = q.z; a0 = fma(x, x, a0);
+            x = q.w; a1 = fma(x, x, a1);
+        }
+        if ((uint32_t)tid < sg.tail) {
+            const double x = g[sg.head + 4 * (size_t)sg.nvec + tid];
+            a1 = fma(x, x, a1);
+        }
+    }
+}
+
+// Statistics of the pending update, computed once in fp64 by one thread.
+__device__ void finalize_stats(DevState* st, double sumsq) {
+    const double D = st->grad_divisor;
+    const double M = st->max_norm;
+    const double norm = sqrt(sumsq) / D;
+    const double raw = M / (norm + 1e-6);
+    const double coef = (raw > 1.0) ? 1.0 : raw;   // NaN stays NaN
+    const double scale = coef / D;
+    st->stats.sumsq = sumsq;
+    st->stats.norm = norm;
+    st->stats.clip_coef = coef;
+    st->stats.grad_scale = scale;
+    st->stats.nonfinite = isfinite(sumsq) ? 0 : 1;
+    st->stats.n_groups = st->n_groups;
+    st->grad_scale_f32 = (float)scale;
+}
+
+// Group k's update count and bias-corrected constants (fp64, rounded once).
+__device__ void finalize_group(DevState* st, int k, int advance) {
+    int64_t t = st->step[k];
+    if (advance) {
+        t += 1;
+        st->step[k] = t;
+    }
+    const somaopt_group h = st->hyper[k];
+    const double bc1 = 1.0 - pow(h.beta1, (double)t);
+    const double bc2 = 1.0 - pow(h.beta2, (double)t);
+    GroupConst c;
+    c.step_size = (float)(h.lr / bc1);
+    c.inv_sqrt_bc2 = (float)(1.0 / sqrt(bc2));
+    c.lr_wd = (float)(h.lr * h.weight_decay);
+    c.beta1 = (float)h.beta1;
+    c.one_minus_beta1 = (float)(1.0 - h.beta1);
+    c.beta2 = (float)h.beta2;
+    c.one_minus_beta2 = (float)(1.0 - h.beta2);
+    c.eps = (float)h.eps;
+    st->gconst[k] = c;
+}
+
+template <int BS>
+__global__ __launch_bounds__(BS) void sqnorm_pass1(Pass1Args a) {
+    __shared__ double lds[BS / 64];
+    __shared__ int is_last;
+    const int tid = threadIdx.x;
+    const uint32_t b = blockIdx.x;
+    const AS_CONST uint32_t* blk = cptr<uint32_t>(a.blk_first);
+    const AS_CONST Seg1* segs = cptr<Seg1>(a.segs);
+    const uint32_t s0 = blk[b];
+    const uint32_t s1 = blk[b + 1];
+    double a0 = 0.0, a1 = 0.0;
+    for (uint32_t s = s0; s < s1; ++s) {
+        const Seg1 sg = cload(segs + s);
+        segment_sumsq<BS>(sg, tid, a0, a1);
+    }
+    const double part = block_sum<BS>(a0 + a1, lds);
+    if (tid == 0) {
+        unsigned long long* slot = reinterpret_cast<unsigned long long*>(a.partials + b);
+        __hip_atomic_store(slot, (unsigned long long)__double_as_longlong(part), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t prev =
+            __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        is_last = (prev == a.n_blocks - 1) ? 1 : 0;
+    }
+    __syncthreads();
+    if (!is_last) return;
+    __threadfence();
+    // Last workgroup: fixed-order sum of all partials, then the statistics.
+    double acc = 0.0;
+    for (uint32_t i = tid; i < a.n_blocks; i += BS) {
+        const unsigned long long bits = __hip_atomic_load(
+            reinterpret_cast<unsigned long long*>(a.partials + i), __ATOMIC_RELAXED,
+            __HIP_MEMORY_SCOPE_AGENT);
+        acc += __longlong_as_double((long long)bits);
+    }
+    const double total = block_sum<BS>(acc, lds);
+    if (tid == 0) {
+        finalize_stats(a.state, total);
+        __hip_atomic_store(a.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (tid < a.n_groups) finalize_group(a.state, tid, a.advance);
+}
+
+// ------------------------------------------------------------------ pass 2
+
+// One element of the fused update: normalize + clip (scale = c / D), AdamW
+// moments, bias-corrected step, decoupled decay of the pre-update weight.
+// p is written as p + (-lr*wd*p - u) with the bracket in one fma, so the
+// weight takes a single rounding at its own scale.
+__device__ __forceinline__ void adamw_elem(float& p, float& m, float& v, float g, const GroupConst& c,
+                                           float scale) {
+    const float gh = g * scale;
+    m = fmaf(c.beta1, m, c.one_minus_beta1 * gh);
+    v = fmaf(c.beta2, v, (c.one_minus_beta2 * gh) * gh);
+    const float denom = fmaf(sqrtf(v), c.inv_sqrt_bc2, c.eps);
+    const float u = c.step_size * (m / denom);
+    p = p + fmaf(-c.lr_wd, p, -u);
+}
+
+__device__ __forceinline__ void adamw_vec(f32x4& p, f32x4& m, f32x4& v, const f32x4& g,
+                                          const GroupConst& c, float scale) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        float pk = p[k], mk = m[k], vk = v[k];
+        adamw_elem(pk, mk, vk, g[k], c, scale);
+        p[k] = pk;
+        m[k] = mk;
+        v[k] = vk;
+    }
+}
+
+template <bool BF16>
+__device__ __forceinline__ f32x4 load_g4(const AS_GLOBAL char* gbase, uint32_t i) {
+    if constexpr (BF16) {
+        const u32x2 w = ((const AS_GLOBAL u32x2*)gbase)[i];
+        f32x4 r;
+        r.x = bf16_lo(w.x);
+        r.y = bf16_hi(w.x);
+        r.z = bf16_lo(w.y);
+        r.w = bf16_hi(w.y);
+        return r;
+    } else {
+        return ((const AS_GLOBAL f32x4*)gbase)[i];
+    }
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load_g1(const AS_GLOBAL char* gbase, size_t i) {
+    if constexpr (BF16) {
+        return bf16_one(((const AS_GLOBAL uint16_t*)gbase)[i]);
+    } else {
+        return ((const AS_GLOBAL float*)gbase)[i];
+    }
+}
+
+template <int BS, bool BF16>
+__device__ __forceinline__ void update_segment(const Seg2& sg, const GroupConst& c, float scale, int tid) {
+    constexpr size_t kGsz = BF16 ? 2 : 4;
+    AS_GLOBAL float* p = gptr<float>(sg.p);
+    AS_GLOBAL float* m = gptr<float>(sg.m);
+    AS_GLOBAL float* v = gptr<float>(sg.v);
+    const AS_GLOBAL char* gb = gptr<char>(sg.g);
+    if ((uint32_t)tid < sg.head) {
+        float pp = p[tid], mm = m[tid], vv = v[tid];
+        adamw_elem(pp, mm, vv, load_g1<BF16>(gb, tid), c, scale);
+        p[tid] = pp;
+        m[tid] = mm;
+        v[tid] = vv;
+    }
+    AS_GLOBAL f32x4* pv = (AS_GLOBAL f32x4*)(p + sg.head);
+    AS_GLOBAL f32x4* mv = (AS_GLOBAL f32x4*)(m + sg.head);
+    AS_GLOBAL f32x4* vv = (AS_GLOBAL f32x4*)(v + sg.head);
+    const AS_GLOBAL char* gv = gb + sg.head * kGsz;
+    const uint32_t nvec = sg.nvec;
+    uint32_t i = tid;
+    for (; i + BS < nvec; i += 2 * BS) {
+        const uint32_t j = i + BS;
+        f32x4 p0 = pv[i], p1 = pv[j];
+        f32x4 m0 = mv[i], m1 = mv[j];
+        f32x4 v0 = vv[i], v1 = vv[j];
+        const f32x4 g0 = load_g4<BF16>(gv, i);
+        const f32x4 g1 = load_g4<BF16>(gv, j);
+        adamw_vec(p0, m0, v0, g0, c, scale);
+        adamw_vec(p1, m1, v1, g1, c, scale);
+        pv[i] = p0;
+        mv[i] = m0;
+        vv[i] = v0;
+        pv[j] = p1;
+        mv[j] = m1;
+        vv[j] = v1;
+    }
+    if (i < nvec) {
+        f32x4 p0 = pv[i], m0 = mv[i], v0 = vv[i];
+        const f32x4 g0 = load_g4<BF16>(gv, i);
+        adamw_vec(p0, m0, v0, g0, c, scale);
+        pv[i] = p0;
+        mv[i] = m0;
+        vv[i] = v0;
+    }
+    if ((uint32_t)tid < sg.tail) {
+        const size_t k = sg.head + 4 * (size_t)nvec + tid;
+        float pp = p[k], mm = m[k], vq = v[k];
+        adamw_elem(pp, mm, vq, load_g1<BF16>(gb, k), c, scale);
+        p[k] = pp;
+        m[k] = mm;
+        v[k] = vq;
+    }
+}
+
+template <int BS>
+__global__ __launch_bounds__(BS) void adamw_pass2(Pass2Args a) {
+    const int tid = threadIdx.x;
+    const uint32_t b = blockIdx.x;
+    const AS_CONST DevState* st = cptr<DevState>(a.state);
+    const AS_CONST uint32_t* blk = cptr<uint32_t>(a.blk_first);
+    const AS_CONST Seg2* segs = cptr<Seg2>(a.segs);
+    const float scale = st->grad_scale_f32;
+    const uint32_t s0 = blk[b];
+    const uint32_t s1 = blk[b + 1];
+    for (uint32_t s = s0; s < s1; ++s) {
+        const Seg2 sg = cload(segs + s);
+        const GroupConst c = cload(&st->gconst[sg.group]);
+        if (sg.dtype == SOMAOPT_BF16)
+            update_segment<BS, true>(sg, c, scale, tid);
+        else
+            update_segment<BS, false>(sg, c, scale, tid);
+    }
+}
+
+// ------------------------------------------------------------- small setters
+
+__global__ void set_groups_kernel(DevState* st, GroupArgs g) {
+    const int k = threadIdx.x;
+    if (k < g.n) st->hyper[k] = g.g[k];
+}
+
+__global__ void set_clip_kernel(DevState* st, double max_norm, double grad_divisor) {
+    if (threadIdx.x == 0) {
+        st->max_norm = max_norm;
+        st->grad_divisor = grad_divisor;
+    }
+}
+
+__global__ void set_step_kernel(DevState* st, int64_t step, int32_t n) {
+    const int k = threadIdx.x;
+    if (k < n) st->step[k] = step;
+}
+
+}  // namespace
+
+hipError_t launch_pass1(const Pass1Args& a, hipStream_t s) {
+    hipLaunchKernelGGL(sqnorm_pass1<kPass1Threads>, dim3(a.n_blocks), dim3(kPass1Threads), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_pass2(const Pass2Args& a, hipStream_t s) {
+    hipLaunchKernelGGL(adamw_pass2<kPass2Threads>, dim3(a.n_blocks), dim3(kPass2Threads), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_set_groups(DevState* st, const GroupArgs& g, hipStream_t s) {
+    hipLaunchKernelGGL(set_groups_kernel, dim3(1), dim3(SOMAOPT_MAX_GROUPS), 0, s, st, g);
+    return hipGetLastError();
+}
+
+hipError_t launch_set_clip(DevState* st, double max_norm, double grad_divisor, hipStream_t s) {
+    hipLaunchKernelGGL(set_clip_kernel, dim3(1), dim3(64), 0, s, st, max_norm, grad_divisor);
+    return hipGetLastError();
+}
+
+hipError_t launch_set_step(DevState* st, int64_t step, int32_t n_groups, hipStream_t s) {
+    hipLaunchKernelGGL(set_step_kernel, dim3(1), dim3(SOMAOPT_MAX_GROUPS), 0, s, st, step, n_groups);
+    return hipGetLastError();
+}
+
+}  // namespace somaopt

@@ -1,0 +1,203 @@
+// Tensor-table planner (host only, no HIP calls).  See plan.hpp.
+#include "plan.hpp"
+
+#include <algorithm>
+#include <cstdio>
+#include <limits>
+
+namespace somaopt {
+
+namespace {
+
+struct Interval {
+    uintptr_t lo, hi;   // [lo, hi)
+    int64_t tensor;
+    int kind;           // 0 p, 1 m, 2 v, 3 g
+};
+
+const char* kKindName[4] = {"param", "exp_avg", "exp_avg_sq", "grad"};
+
+std::string fmt(const char* f, long long a = 0, long long b = 0, long long c = 0) {
+    char buf[256];
+    std::snprintf(buf, sizeof(buf), f, a, b, c);
+    return buf;
+}
+
+}  // namespace
+
+int64_t normalise_chunk(int64_t requested, int64_t dflt) {
+    int64_t c = requested > 0 ? requested : dflt;
+    c = (c / 8) * 8;
+    if (c < 256) c = 256;
+    if (c > (int64_t(1) << 30)) c = int64_t(1) << 30;
+    return c;
+}
+
+int validate_host(const somaopt_tensor_desc* d, int64_t n, int32_t n_groups, std::string& err,
+                  Counts* counts) {
+    if (n < 0) { err = "n_tensors < 0"; return SOMAOPT_E_INVALID; }
+    if (n > 0 && d == nullptr) { err = "descs is NULL"; return SOMAOPT_E_INVALID; }
+    if (n_groups < 1 || n_groups > SOMAOPT_MAX_GROUPS) {
+        err = fmt("n_groups=%lld outside [1, %lld]", n_groups, SOMAOPT_MAX_GROUPS);
+        return SOMAOPT_E_INVALID;
+    }
+    Counts c;
+    std::vector<Interval> iv;
+    for (int64_t i = 0; i < n; ++i) {
+        const somaopt_tensor_desc& t = d[i];
+        if (t.trainable != 0 && t.trainable != 1) {
+            err = fmt("tensor %lld: trainable must be 0 or 1", i);
+            return SOMAOPT_E_INVALID;
+        }
+        if (!t.trainable) continue;   // frozen: never read, never validated further
+        if (t.owner != 0 && t.owner != 1) {
+            err = fmt("tensor %lld: owner must be 0 or 1", i);
+            return SOMAOPT_E_INVALID;
+        }
+        if (t.numel < 0) { err = fmt("tensor %lld: numel %lld < 0", i, t.numel); return SOMAOPT_E_INVALID; }
+        if (t.numel > (int64_t(1) << 40)) { err = fmt("tensor %lld: numel too large", i); return SOMAOPT_E_INVALID; }
+        if (t.grad_dtype != SOMAOPT_F32 && t.grad_dtype != SOMAOPT_BF16) {
+            err = fmt("tensor %lld: unknown grad_dtype %lld", i, t.grad_dtype);
+            return SOMAOPT_E_INVALID;
+        }
+        if (t.group < 0 || t.group >= n_groups) {
+            err = fmt("tensor %lld: group %lld outside [0, %lld)", i, t.group, n_groups);
+            return SOMAOPT_E_INVALID;
+        }
+        c.n_trainable++;
+        c.trainable_numel += t.numel;
+        if (t.owner) c.owned_numel += t.numel;
+        if (t.numel == 0) continue;
+        const void* ptrs[4] = {t.param, t.exp_avg, t.exp_avg_sq, t.grad};
+        const int64_t esz[4] = {4, 4, 4, grad_elem_bytes(t.grad_dtype)};
+        for (int k = 0; k < 4; ++k) {
+            uintptr_t a = reinterpret_cast<uintptr_t>(ptrs[k]);
+            if (a == 0) {
+                err = std::string("tensor ") + std::to_string(i) + ": " + kKindName[k] + " pointer is NULL";
+                return SOMAOPT_E_INVALID;
+            }
+            if (a % (uintptr_t)esz[k]) {
+                err = std::string("tensor ") + std::to_string(i) + ": " + kKindName[k] +
+                      " pointer is not aligned to its element size";
+                return SOMAOPT_E_INVALID;
+            }
+            uintptr_t bytes = (uintptr_t)t.numel * (uintptr_t)esz[k];
+            if (a + bytes < a) {
+                err = std::string("tensor ") + std::to_string(i) + ": " + kKindName[k] + " range wraps";
+                return SOMAOPT_E_INVALID;
+            }
+            iv.push_back(Interval{a, a + bytes, i, k});
+        }
+    }
+    // Overlap check: writable buffers (p, m, v) may overlap nothing; gradients
+    // may overlap other gradients (both read-only) but no p/m/v buffer.
+    std::sort(iv.begin(), iv.end(), [](const Interval& x, const Interval& y) {
+        return x.lo < y.lo || (x.lo == y.lo && x.hi < y.hi);
+    });
+    // Sweep keeping the interval with the furthest end among writable ones and
+    // among gradients separately.
+    uintptr_t w_end = 0, g_end = 0;
+    int64_t w_t = -1, g_t = -1;
+    int w_k = 0, g_k = 0;
+    for (const Interval& x : iv) {
+        bool writable = x.kind != 3;
+        if (w_t >= 0 && x.lo < w_end) {
+            err = std::string("buffers overlap: tensor ") + std::to_string(x.tensor) + " " +
+                  kKindName[x.kind] + " and tensor " + std::to_string(w_t) + " " + kKindName[w_k];
+            return SOMAOPT_E_INVALID;
+        }
+        if (writable && g_t >= 0 && x.lo < g_end) {
+            err = std::string("buffers overlap: tensor ") + std::to_string(x.tensor) + " " +
+                  kKindName[x.kind] + " and tensor " + std::to_string(g_t) + " " + kKindName[g_k];
+            return SOMAOPT_E_INVALID;
+        }
+        if (writable) {
+            if (x.hi > w_end || w_t < 0) { w_end = x.hi; w_t = x.tensor; w_k = x.kind; }
+        } else {
+            if (x.hi > g_end || g_t < 0) { g_end = x.hi; g_t = x.tensor; g_k = x.kind; }
+        }
+    }
+    if (counts) *counts = c;
+    return SOMAOPT_OK;
+}
+
+namespace {
+
+// Smallest e in [0, vec) such that every listed address, advanced by e
+// elements of its size, is aligned to `vec * size`; -1 if none exists.
+int64_t common_head(const uintptr_t* addr, const int64_t* esz, int n, int64_t vec) {
+    for (int64_t e = 0; e < vec; ++e) {
+        bool ok = true;
+        for (int k = 0; k < n && ok; ++k) {
+            uintptr_t need = (uintptr_t)(vec * esz[k]);
+            ok = ((addr[k] + (uintptr_t)(e * esz[k])) % need) == 0;
+        }
+        if (ok) return e;
+    }
+    return -1;
+}
+
+}  // namespace
+
+Plan build_plan(const somaopt_tensor_desc* d, int64_t n, int pass, int64_t chunk) {
+    Plan plan;
+    plan.chunk = chunk;
+    for (int64_t i = 0; i < n; ++i) {
+        const somaopt_tensor_desc& t = d[i];
+        if (!t.trainable || t.numel == 0) continue;
+        if (pass == 1 && !t.owner) continue;
+        const int64_t gsz = grad_elem_bytes(t.grad_dtype);
+        int64_t vec, head;
+        if (pass == 1) {
+            vec = 16 / gsz;
+            uintptr_t a[1] = {reinterpret_cast<uintptr_t>(t.grad)};
+            int64_t s[1] = {gsz};
+            head = common_head(a, s, 1, vec);
+        } else {
+            vec = 4;
+            uintptr_t a[4] = {reinterpret_cast<uintptr_t>(t.param), reinterpret_cast<uintptr_t>(t.exp_avg),
+                              reinterpret_cast<uintptr_t>(t.exp_avg_sq), reinterpret_cast<uintptr_t>(t.grad)};
+            int64_t s[4] = {4, 4, 4, gsz};
+            head = common_head(a, s, 4, vec);
+        }
+        if (head < 0) {
+            // No common alignment: the whole tensor takes the scalar path.
+            for (int64_t off = 0; off < t.numel; off += chunk) {
+                int64_t len = std::min(chunk, t.numel - off);
+                plan.segs.push_back(PlanSeg{i, off, len, 0, (int32_t)len, 0, 0, -1});
+            }
+            continue;
+        }
+        head = std::min(head, t.numel);
+        int64_t off = 0;
+        bool first = true;
+        while (off < t.numel) {
+            int64_t h = first ? head : 0;
+            int64_t room = first ? ((chunk - h) / vec) * vec : chunk;   // body capacity
+            int64_t body = std::min(room, t.numel - off - h);
+            int64_t nv = body / vec;
+            int64_t tl = body - nv * vec;
+            int64_t len = h + body;
+            plan.segs.push_back(PlanSeg{i, off, len, nv, (int32_t)h, (int32_t)tl, (int32_t)vec, -1});
+            off += len;
+            first = false;
+        }
+    }
+    // Pack consecutive segments into workgroups of bounded cost.
+    plan.block_first.clear();
+    int64_t cost = 0;
+    for (size_t s = 0; s < plan.segs.size(); ++s) {
+        int64_t c = plan.segs[s].numel + kSegmentCost;
+        if (plan.block_first.empty() || cost + c > chunk + kSegmentCost) {
+            plan.block_first.push_back((uint32_t)s);
+            cost = 0;
+        }
+        cost += c;
+        plan.segs[s].block = (int32_t)(plan.block_first.size() - 1);
+    }
+    plan.block_first.push_back((uint32_t)plan.segs.size());
+    if (plan.segs.empty()) plan.block_first.assign(1, 0);
+    return plan;
+}
+
+}  // namespace somaopt

@@ -1,0 +1,81 @@
+// Host-side tensor-table planner: validation, frozen-tensor removal, alignment
+// analysis and the split of every tensor into workgroup-sized segments.
+//
+// The landing page's fused optimizer batches the norm and update work across
+// tensors instead of launching per tensor (paragraph "SomaSpeed batches that
+// work across tensors ..."); here that batching is a device-resident segment
+// table plus a block table, built once by this planner.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "somaopt.h"
+
+namespace somaopt {
+
+// Device layout of a norm-pass segment: a contiguous run of one owned gradient.
+struct alignas(8) Seg1 {
+    const void* g;      // first element of the segment
+    uint32_t head;      // scalar elements before the first 16-byte vector
+    uint32_t nvec;      // 16-byte vectors (4 fp32 or 8 bf16 elements)
+    uint32_t tail;      // scalar elements after the last vector
+    uint32_t dtype;     // somaopt_dtype
+};
+static_assert(sizeof(Seg1) == 24, "Seg1 layout");
+
+// Device layout of an update-pass segment: the same run of p, m, v and g.
+struct alignas(16) Seg2 {
+    float* p;
+    float* m;
+    float* v;
+    const void* g;
+    uint32_t head;      // scalar elements before the first 4-element vector
+    uint32_t nvec;      // 4-element vectors (16 bytes of p/m/v, 8 or 16 of g)
+    uint32_t tail;      // scalar elements after the last vector
+    uint16_t group;
+    uint16_t dtype;
+};
+static_assert(sizeof(Seg2) == 48, "Seg2 layout");
+
+constexpr int64_t kDefaultPass1Chunk = 32768;
+constexpr int64_t kDefaultPass2Chunk = 8192;
+constexpr int64_t kSegmentCost = 64;   // packing cost of one segment, in elements
+
+struct PlanSeg {
+    int64_t tensor;
+    int64_t offset;
+    int64_t numel;
+    int64_t nvec;
+    int32_t head;
+    int32_t tail;
+    int32_t vec;      // elements per vector, 0 = scalar only
+    int32_t block;
+};
+
+struct Plan {
+    std::vector<PlanSeg> segs;
+    std::vector<uint32_t> block_first;   // n_blocks + 1 entries
+    int64_t chunk = 0;
+    int64_t n_blocks() const { return (int64_t)block_first.size() - 1; }
+};
+
+struct Counts {
+    int64_t n_trainable = 0, trainable_numel = 0, owned_numel = 0;
+};
+
+// Validation that needs no device.  Returns SOMAOPT_OK or SOMAOPT_E_INVALID with
+// `err` set.
+int validate_host(const somaopt_tensor_desc* d, int64_t n, int32_t n_groups, std::string& err,
+                  Counts* counts);
+
+// pass = 1 (owned gradient segments) or 2 (all trainable segments).
+Plan build_plan(const somaopt_tensor_desc* d, int64_t n, int pass, int64_t chunk);
+
+// Normalise a requested chunk: positive multiple of 8, at least 256 elements.
+int64_t normalise_chunk(int64_t requested, int64_t dflt);
+
+inline int64_t grad_elem_bytes(int32_t dtype) { return dtype == SOMAOPT_BF16 ? 2 : 4; }
+
+}  // namespace somaopt

@@ -1,0 +1,477 @@
+// C-ABI of the fused clip + AdamW optimizer step (declared in include/somaopt.h).
+//
+// Host side only: argument validation, the device tables built once at init,
+// stream-ordered launches of the two passes and of the small setters, and the
+// HIP-graph capture / replay of a whole step.  All arithmetic of the step runs
+// in the kernels (kernels.hip).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "kernels.hpp"
+#include "plan.hpp"
+#include "somaopt.h"
+#include "state.hpp"
+
+using namespace somaopt;
+
+struct somaopt_handle {
+    int device = -1;
+    int32_t n_groups = 0;
+    somaopt_plan_info info{};
+    Seg1* d_seg1 = nullptr;
+    uint32_t* d_blk1 = nullptr;
+    uint32_t nblk1 = 0;
+    Seg2* d_seg2 = nullptr;
+    uint32_t* d_blk2 = nullptr;
+    uint32_t nblk2 = 0;
+    double* d_partials = nullptr;
+    uint32_t* d_ticket = nullptr;
+    DevState* d_state = nullptr;
+    bool pending = false;          // a norm pass opened an update not yet applied
+    hipStream_t cap_stream = nullptr;
+    hipGraphExec_t exec = nullptr;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+    g_last_error = msg;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(SOMAOPT_E_HIP, std::string(what) + ": " + hipGetErrorName(e) + " (" +
+                                   hipGetErrorString(e) + ")");
+}
+
+// Makes the handle's device current for the duration of a call.
+class DeviceGuard {
+   public:
+    explicit DeviceGuard(int dev) {
+        if (hipGetDevice(&prev_) != hipSuccess) prev_ = -1;
+        if (prev_ != dev) ok_ = hipSetDevice(dev) == hipSuccess;
+        restore_ = prev_ >= 0 && prev_ != dev;
+    }
+    ~DeviceGuard() {
+        if (restore_) (void)hipSetDevice(prev_);
+    }
+    bool ok() const { return ok_; }
+
+   private:
+    int prev_ = -1;
+    bool ok_ = true;
+    bool restore_ = false;
+};
+
+bool finite(double x) { return std::isfinite(x); }
+
+int check_groups(const somaopt_group* g, int32_t n) {
+    if (n < 1 || n > SOMAOPT_MAX_GROUPS)
+        return fail(SOMAOPT_E_INVALID, "n_groups must be in [1, " + std::to_string(SOMAOPT_MAX_GROUPS) + "]");
+    if (!g) return fail(SOMAOPT_E_INVALID, "groups is NULL");
+    for (int32_t k = 0; k < n; ++k) {
+        const somaopt_group& h = g[k];
+        const std::string at = "group " + std::to_string(k) + ": ";
+        if (!finite(h.lr)) return fail(SOMAOPT_E_INVALID, at + "lr is not finite");
+        if (!finite(h.weight_decay)) return fail(SOMAOPT_E_INVALID, at + "weight_decay is not finite");
+        if (!(h.beta1 >= 0.0 && h.beta1 < 1.0)) return fail(SOMAOPT_E_INVALID, at + "beta1 outside [0, 1)");
+        if (!(h.beta2 >= 0.0 && h.beta2 < 1.0)) return fail(SOMAOPT_E_INVALID, at + "beta2 outside [0, 1)");
+        if (!(h.eps >= 0.0) || !finite(h.eps)) return fail(SOMAOPT_E_INVALID, at + "eps must be finite and >= 0");
+    }
+    return SOMAOPT_OK;
+}
+
+int check_clip(double max_norm, double grad_divisor) {
+    if (!(max_norm > 0.0) || !finite(max_norm)) return fail(SOMAOPT_E_INVALID, "max_norm must be finite and > 0");
+    if (!(grad_divisor > 0.0) || !finite(grad_divisor))
+        return fail(SOMAOPT_E_INVALID, "grad_divisor must be finite and > 0");
+    return SOMAOPT_OK;
+}
+
+int64_t env_int(const char* name, int64_t dflt) {
+    const char* s = std::getenv(name);
+    if (!s || !*s) return dflt;
+    char* end = nullptr;
+    long long v = std::strtoll(s, &end, 10);
+    return (end && *end == 0) ? (int64_t)v : dflt;
+}
+
+// Every trainable buffer must be device memory of `dev` and lie inside one
+// allocation, so that no kernel can address memory it was not given.
+int check_pointers(const somaopt_tensor_desc* d, int64_t n, int dev) {
+    const char* skip = std::getenv("SOMAOPT_SKIP_POINTER_CHECK");
+    if (skip && std::strcmp(skip, "1") == 0) return SOMAOPT_OK;
+    static const char* kind[4] = {"param", "exp_avg", "exp_avg_sq", "grad"};
+    for (int64_t i = 0; i < n; ++i) {
+        const somaopt_tensor_desc& t = d[i];
+        if (!t.trainable || t.numel == 0) continue;
+        const void* ptrs[4] = {t.param, t.exp_avg, t.exp_avg_sq, t.grad};
+        const size_t esz[4] = {4, 4, 4, (size_t)grad_elem_bytes(t.grad_dtype)};
+        for (int k = 0; k < 4; ++k) {
+            const std::string at = "tensor " + std::to_string(i) + " " + kind[k] + ": ";
+            hipPointerAttribute_t attr;
+            std::memset(&attr, 0, sizeof(attr));
+            hipError_t e = hipPointerGetAttributes(&attr, ptrs[k]);
+            if (e != hipSuccess) {
+                (void)hipGetLastError();
+                return fail(SOMAOPT_E_INVALID, at + "not a HIP device pointer");
+            }
+            if (attr.type != hipMemoryTypeDevice || attr.device != dev)
+                return fail(SOMAOPT_E_INVALID, at + "not device memory of the current device");
+            hipDeviceptr_t base = nullptr;
+            size_t size = 0;
+            e = hipMemGetAddressRange(&base, &size, const_cast<void*>(ptrs[k]));
+            if (e != hipSuccess) {
+                (void)hipGetLastError();
+                return fail(SOMAOPT_E_INVALID, at + "allocation range unknown to HIP");
+            }
+            const uintptr_t lo = reinterpret_cast<uintptr_t>(base);
+            const uintptr_t a = reinterpret_cast<uintptr_t>(ptrs[k]);
+            const uintptr_t bytes = (uintptr_t)t.numel * esz[k];
+            if (a < lo || a + bytes > lo + size)
+                return fail(SOMAOPT_E_INVALID, at + "runs past the end of its allocation");
+        }
+    }
+    return SOMAOPT_OK;
+}
+
+void free_handle(somaopt_handle* h) {
+    if (!h) return;
+    if (h->exec) (void)hipGraphExecDestroy(h->exec);
+    if (h->cap_stream) (void)hipStreamDestroy(h->cap_stream);
+    void* bufs[] = {h->d_seg1, h->d_blk1, h->d_seg2, h->d_blk2, h->d_partials, h->d_ticket, h->d_state};
+    for (void* p : bufs)
+        if (p) (void)hipFree(p);
+    delete h;
+}
+
+template <typename T>
+hipError_t alloc_upload(T** dst, const std::vector<T>& src, hipStream_t s) {
+    const size_t bytes = std::max<size_t>(src.size(), 1) * sizeof(T);
+    hipError_t e = hipMalloc(reinterpret_cast<void**>(dst), bytes);
+    if (e != hipSuccess) return e;
+    if (!src.empty()) e = hipMemcpyAsync(*dst, src.data(), src.size() * sizeof(T), hipMemcpyHostToDevice, s);
+    return e;
+}
+
+void fill_info(somaopt_plan_info* info, int64_t n_tensors, const Counts& c, const Plan& p1, const Plan& p2) {
+    std::memset(info, 0, sizeof(*info));
+    info->n_tensors = n_tensors;
+    info->n_trainable = c.n_trainable;
+    info->trainable_numel = c.trainable_numel;
+    info->owned_numel = c.owned_numel;
+    info->pass1_segments = (int64_t)p1.segs.size();
+    info->pass1_blocks = p1.n_blocks();
+    info->pass2_segments = (int64_t)p2.segs.size();
+    info->pass2_blocks = p2.n_blocks();
+    int64_t scal = 0;
+    for (const PlanSeg& s : p2.segs) scal += (s.vec == 0);
+    info->scalar_segments = scal;
+    info->pass1_chunk = p1.chunk;
+    info->pass2_chunk = p2.chunk;
+    info->table_bytes = (int64_t)(p1.segs.size() * sizeof(Seg1) + p2.segs.size() * sizeof(Seg2) +
+                                  (p1.block_first.size() + p2.block_first.size()) * sizeof(uint32_t));
+}
+
+int launch_norm_pass(somaopt_handle* h, int advance, hipStream_t s) {
+    Pass1Args a;
+    a.segs = h->d_seg1;
+    a.blk_first = h->d_blk1;
+    a.n_blocks = h->nblk1;
+    a.partials = h->d_partials;
+    a.ticket = h->d_ticket;
+    a.state = h->d_state;
+    a.n_groups = h->n_groups;
+    a.advance = advance;
+    hipError_t e = launch_pass1(a, s);
+    return e == hipSuccess ? SOMAOPT_OK : hip_fail(e, "norm pass launch");
+}
+
+int launch_update_pass(somaopt_handle* h, hipStream_t s) {
+    if (h->nblk2 == 0) return SOMAOPT_OK;
+    Pass2Args a;
+    a.segs = h->d_seg2;
+    a.blk_first = h->d_blk2;
+    a.n_blocks = h->nblk2;
+    a.state = h->d_state;
+    hipError_t e = launch_pass2(a, s);
+    return e == hipSuccess ? SOMAOPT_OK : hip_fail(e, "update pass launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* somaopt_last_error(void) { return g_last_error.c_str(); }
+
+const char* somaopt_version(void) { return "somaopt 0.1.0 (gfx950)"; }
+
+int64_t somaopt_debug_plan(const somaopt_tensor_desc* descs, int64_t n_tensors, int32_t n_groups,
+                           int32_t pass, int64_t pass1_chunk, int64_t pass2_chunk,
+                           somaopt_plan_segment* segs, int64_t cap, somaopt_plan_info* info) {
+    if (pass != 1 && pass != 2) return fail(SOMAOPT_E_INVALID, "pass must be 1 or 2");
+    if (cap < 0) return fail(SOMAOPT_E_INVALID, "cap < 0");
+    std::string err;
+    Counts c;
+    int rc = validate_host(descs, n_tensors, n_groups, err, &c);
+    if (rc != SOMAOPT_OK) return fail(rc, err);
+    const int64_t ch1 = normalise_chunk(pass1_chunk, kDefaultPass1Chunk);
+    const int64_t ch2 = normalise_chunk(pass2_chunk, kDefaultPass2Chunk);
+    Plan p1 = build_plan(descs, n_tensors, 1, ch1);
+    Plan p2 = build_plan(descs, n_tensors, 2, ch2);
+    if (info) fill_info(info, n_tensors, c, p1, p2);
+    const Plan& p = pass == 1 ? p1 : p2;
+    if (segs) {
+        for (int64_t i = 0; i < (int64_t)p.segs.size() && i < cap; ++i) {
+            const PlanSeg& s = p.segs[i];
+            segs[i].tensor = s.tensor;
+            segs[i].offset = s.offset;
+            segs[i].numel = s.numel;
+            segs[i].nvec = s.nvec;
+            segs[i].head = s.head;
+            segs[i].tail = s.tail;
+            segs[i].vec_elems = s.vec;
+            segs[i].block = s.block;
+        }
+    }
+    return (int64_t)p.segs.size();
+}
+
+int somaopt_init_tensor_table(const somaopt_tensor_desc* descs, int64_t n_tensors,
+                              const somaopt_group* groups, int32_t n_groups, double max_norm,
+                              double grad_divisor, int64_t initial_step, void* stream,
+                              somaopt_handle** out) {
+    if (!out) return fail(SOMAOPT_E_INVALID, "out is NULL");
+    *out = nullptr;
+    int rc = check_groups(groups, n_groups);
+    if (rc) return rc;
+    if ((rc = check_clip(max_norm, grad_divisor))) return rc;
+    if (initial_step < 0) return fail(SOMAOPT_E_INVALID, "initial_step < 0");
+    std::string err;
+    Counts counts;
+    rc = validate_host(descs, n_tensors, n_groups, err, &counts);
+    if (rc) return fail(rc, err);
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if ((rc = check_pointers(descs, n_tensors, dev))) return rc;
+
+    const int64_t ch1 = normalise_chunk(env_int("SOMAOPT_PASS1_CHUNK", 0), kDefaultPass1Chunk);
+    const int64_t ch2 = normalise_chunk(env_int("SOMAOPT_PASS2_CHUNK", 0), kDefaultPass2Chunk);
+    Plan p1 = build_plan(descs, n_tensors, 1, ch1);
+    Plan p2 = build_plan(descs, n_tensors, 2, ch2);
+    if (p1.segs.size() >= 0xFFFFFFFFull || p2.segs.size() >= 0xFFFFFFFFull)
+        return fail(SOMAOPT_E_INVALID, "too many segments for 32-bit indices");
+    // The norm pass always runs at least one workgroup so that the statistics
+    // are produced even when nothing is owned.
+    if (p1.block_first.size() < 2) p1.block_first = {0u, 0u};
+
+    std::vector<Seg1> s1(p1.segs.size());
+    for (size_t i = 0; i < p1.segs.size(); ++i) {
+        const PlanSeg& s = p1.segs[i];
+        const somaopt_tensor_desc& t = descs[s.tensor];
+        const size_t gsz = (size_t)grad_elem_bytes(t.grad_dtype);
+        s1[i].g = static_cast<const char*>(t.grad) + (size_t)s.offset * gsz;
+        s1[i].head = (uint32_t)s.head;
+        s1[i].nvec = (uint32_t)s.nvec;
+        s1[i].tail = (uint32_t)s.tail;
+        s1[i].dtype = (uint32_t)t.grad_dtype;
+    }
+    std::vector<Seg2> s2(p2.segs.size());
+    for (size_t i = 0; i < p2.segs.size(); ++i) {
+        const PlanSeg& s = p2.segs[i];
+        const somaopt_tensor_desc& t = descs[s.tensor];
+        const size_t gsz = (size_t)grad_elem_bytes(t.grad_dtype);
+        s2[i].p = static_cast<float*>(t.param) + s.offset;
+        s2[i].m = static_cast<float*>(t.exp_avg) + s.offset;
+        s2[i].v = static_cast<float*>(t.exp_avg_sq) + s.offset;
+        s2[i].g = static_cast<const char*>(t.grad) + (size_t)s.offset * gsz;
+        s2[i].head = (uint32_t)s.head;
+        s2[i].nvec = (uint32_t)s.nvec;
+        s2[i].tail = (uint32_t)s.tail;
+        s2[i].group = (uint16_t)t.group;
+        s2[i].dtype = (uint16_t)t.grad_dtype;
+    }
+
+    DevState st;
+    std::memset(&st, 0, sizeof(st));
+    st.n_groups = n_groups;
+    st.stats.n_groups = n_groups;
+    st.max_norm = max_norm;
+    st.grad_divisor = grad_divisor;
+    for (int32_t k = 0; k < n_groups; ++k) {
+        st.step[k] = initial_step;
+        st.hyper[k] = groups[k];
+    }
+
+    somaopt_handle* h = new (std::nothrow) somaopt_handle();
+    if (!h) return fail(SOMAOPT_E_NOMEM, "host allocation failed");
+    h->device = dev;
+    h->n_groups = n_groups;
+    fill_info(&h->info, n_tensors, counts, p1, p2);
+    h->nblk1 = (uint32_t)(p1.block_first.size() - 1);
+    h->nblk2 = (uint32_t)p2.n_blocks();
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    if ((e = alloc_upload(&h->d_seg1, s1, s)) != hipSuccess ||
+        (e = alloc_upload(&h->d_blk1, p1.block_first, s)) != hipSuccess ||
+        (e = alloc_upload(&h->d_seg2, s2, s)) != hipSuccess ||
+        (e = alloc_upload(&h->d_blk2, p2.block_first, s)) != hipSuccess) {
+        free_handle(h);
+        return e == hipErrorOutOfMemory ? fail(SOMAOPT_E_NOMEM, "device allocation of the tables failed")
+                                        : hip_fail(e, "table upload");
+    }
+    std::vector<DevState> stv(1, st);
+    if ((e = alloc_upload(&h->d_state, stv, s)) != hipSuccess ||
+        (e = hipMalloc(reinterpret_cast<void**>(&h->d_partials), sizeof(double) * std::max<uint32_t>(h->nblk1, 1))) !=
+            hipSuccess ||
+        (e = hipMalloc(reinterpret_cast<void**>(&h->d_ticket), sizeof(uint32_t) * 64)) != hipSuccess ||
+        (e = hipMemsetAsync(h->d_ticket, 0, sizeof(uint32_t) * 64, s)) != hipSuccess ||
+        (e = hipStreamSynchronize(s)) != hipSuccess) {
+        free_handle(h);
+        return e == hipErrorOutOfMemory ? fail(SOMAOPT_E_NOMEM, "device allocation failed")
+                                        : hip_fail(e, "state upload");
+    }
+    *out = h;
+    return SOMAOPT_OK;
+}
+
+int somaopt_grad_sqnorm(somaopt_handle* h, void* stream) {
+    if (!h) return fail(SOMAOPT_E_INVALID, "handle is NULL");
+    DeviceGuard g(h->device);
+    if (!g.ok()) return fail(SOMAOPT_E_HIP, "cannot select the handle's device");
+    int rc = launch_norm_pass(h, h->pending ? 0 : 1, static_cast<hipStream_t>(stream));
+    if (rc) return rc;
+    h->pending = true;
+    return SOMAOPT_OK;
+}
+
+int somaopt_fused_adamw_step(somaopt_handle* h, void* stream) {
+    if (!h) return fail(SOMAOPT_E_INVALID, "handle is NULL");
+    if (!h->pending) return fail(SOMAOPT_E_STATE, "somaopt_grad_sqnorm must precede each update");
+    DeviceGuard g(h->device);
+    if (!g.ok()) return fail(SOMAOPT_E_HIP, "cannot select the handle's device");
+    int rc = launch_update_pass(h, static_cast<hipStream_t>(stream));
+    if (rc) return rc;
+    h->pending = false;
+    return SOMAOPT_OK;
+}
+
+int somaopt_set_groups(somaopt_handle* h, const somaopt_group* groups, int32_t n_groups, void* stream) {
+    if (!h) return fail(SOMAOPT_E_INVALID, "handle is NULL");
+    if (n_groups != h->n_groups) return fail(SOMAOPT_E_INVALID, "n_groups differs from the handle's");
+    int rc = check_groups(groups, n_groups);
+    if (rc) return rc;
+    GroupArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.n = n_groups;
+    for (int32_t k = 0; k < n_groups; ++k) a.g[k] = groups[k];
+    DeviceGuard g(h->device);
+    if (!g.ok()) return fail(SOMAOPT_E_HIP, "cannot select the handle's device");
+    hipError_t e = launch_set_groups(h->d_state, a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SOMAOPT_OK : hip_fail(e, "set_groups launch");
+}
+
+int somaopt_set_clip(somaopt_handle* h, double max_norm, double grad_divisor, void* stream) {
+    if (!h) return fail(SOMAOPT_E_INVALID, "handle is NULL");
+    int rc = check_clip(max_norm, grad_divisor);
+    if (rc) return rc;
+    DeviceGuard g(h->device);
+    if (!g.ok()) return fail(SOMAOPT_E_HIP, "cannot select the handle's device");
+    hipError_t e = launch_set_clip(h->d_state, max_norm, grad_divisor, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SOMAOPT_OK : hip_fail(e, "set_clip launch");
+}
+
+int somaopt_set_step(somaopt_handle* h, int64_t step, void* stream) {
+    if (!h) return fail(SOMAOPT_E_INVALID, "handle is NULL");
+    if (step < 0) return fail(SOMAOPT_E_INVALID, "step < 0");
+    DeviceGuard g(h->device);
+    if (!g.ok()) return fail(SOMAOPT_E_HIP, "cannot select the handle's device");
+    hipError_t e = launch_set_step(h->d_state, step, h->n_groups, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "set_step launch");
+    h->pending = false;
+    return SOMAOPT_OK;
+}
+
+int somaopt_capture_step(somaopt_handle* h) {
+    if (!h) return fail(SOMAOPT_E_INVALID, "handle is NULL");
+    DeviceGuard g(h->device);
+    if (!g.ok()) return fail(SOMAOPT_E_HIP, "cannot select the handle's device");
+    hipError_t e;
+    if (!h->cap_stream) {
+        e = hipStreamCreateWithFlags(&h->cap_stream, hipStreamNonBlocking);
+        if (e != hipSuccess) {
+            h->cap_stream = nullptr;
+            return hip_fail(e, "hipStreamCreateWithFlags");
+        }
+    }
+    e = hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamBeginCapture");
+    int rc = launch_norm_pass(h, 1, h->cap_stream);
+    if (!rc) rc = launch_update_pass(h, h->cap_stream);
+    hipGraph_t graph = nullptr;
+    e = hipStreamEndCapture(h->cap_stream, &graph);
+    if (rc) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return rc;
+    }
+    if (e != hipSuccess) return hip_fail(e, "hipStreamEndCapture");
+    hipGraphExec_t exec = nullptr;
+    e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (e != hipSuccess) return hip_fail(e, "hipGraphInstantiate");
+    if (h->exec) (void)hipGraphExecDestroy(h->exec);
+    h->exec = exec;
+    return SOMAOPT_OK;
+}
+
+int somaopt_replay_step(somaopt_handle* h, void* stream) {
+    if (!h) return fail(SOMAOPT_E_INVALID, "handle is NULL");
+    if (!h->exec) return fail(SOMAOPT_E_STATE, "no captured step (call somaopt_capture_step)");
+    if (h->pending) return fail(SOMAOPT_E_STATE, "an eager norm pass is pending; finish it with somaopt_fused_adamw_step");
+    DeviceGuard g(h->device);
+    if (!g.ok()) return fail(SOMAOPT_E_HIP, "cannot select the handle's device");
+    hipError_t e = hipGraphLaunch(h->exec, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SOMAOPT_OK : hip_fail(e, "hipGraphLaunch");
+}
+
+int somaopt_device_stats(somaopt_handle* h, const void** stats_dev) {
+    if (!h || !stats_dev) return fail(SOMAOPT_E_INVALID, "NULL argument");
+    *stats_dev = &h->d_state->stats;
+    return SOMAOPT_OK;
+}
+
+int somaopt_read_stats(somaopt_handle* h, somaopt_stats* out, int64_t* steps_out, void* stream) {
+    if (!h || !out) return fail(SOMAOPT_E_INVALID, "NULL argument");
+    DeviceGuard g(h->device);
+    if (!g.ok()) return fail(SOMAOPT_E_HIP, "cannot select the handle's device");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(out, &h->d_state->stats, sizeof(somaopt_stats), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess && steps_out)
+        e = hipMemcpyAsync(steps_out, h->d_state->step, sizeof(int64_t) * h->n_groups, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    return e == hipSuccess ? SOMAOPT_OK : hip_fail(e, "read_stats");
+}
+
+int somaopt_get_plan_info(const somaopt_handle* h, somaopt_plan_info* out) {
+    if (!h || !out) return fail(SOMAOPT_E_INVALID, "NULL argument");
+    *out = h->info;
+    return SOMAOPT_OK;
+}
+
+void somaopt_destroy(somaopt_handle* h) {
+    if (!h) return;
+    DeviceGuard g(h->device);
+    (void)hipDeviceSynchronize();
+    free_handle(h);
+}
+
+}  // extern "C"

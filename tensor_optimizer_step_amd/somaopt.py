@@ -1,0 +1,290 @@
+"""ctypes binding of ``libsomaopt.so`` (argument marshalling only).
+
+Every step of the optimizer runs in the library's HIP kernels; this module only
+turns Python values and torch tensors into the C structs and raw device
+pointers that ``include/somaopt.h`` declares.  Loading fails loudly when the
+library has not been built: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Iterable, List, Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsomaopt.so")
+
+F32 = 0
+BF16 = 1
+MAX_GROUPS = 64
+
+OK, E_INVALID, E_HIP, E_NOMEM, E_STATE = 0, -1, -2, -3, -4
+_STATUS = {E_INVALID: "SOMAOPT_E_INVALID", E_HIP: "SOMAOPT_E_HIP", E_NOMEM: "SOMAOPT_E_NOMEM",
+           E_STATE: "SOMAOPT_E_STATE"}
+
+
+class TensorDesc(ctypes.Structure):
+    _fields_ = [("param", ctypes.c_void_p), ("grad", ctypes.c_void_p),
+                ("exp_avg", ctypes.c_void_p), ("exp_avg_sq", ctypes.c_void_p),
+                ("numel", ctypes.c_int64), ("grad_dtype", ctypes.c_int32),
+                ("group", ctypes.c_int32), ("trainable", ctypes.c_int32),
+                ("owner", ctypes.c_int32)]
+
+
+class Group(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("weight_decay", ctypes.c_double),
+                ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("eps", ctypes.c_double)]
+
+
+class Stats(ctypes.Structure):
+    _fields_ = [("sumsq", ctypes.c_double), ("norm", ctypes.c_double),
+                ("clip_coef", ctypes.c_double), ("grad_scale", ctypes.c_double),
+                ("nonfinite", ctypes.c_int32), ("n_groups", ctypes.c_int32)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "n_tensors", "n_trainable", "trainable_numel", "owned_numel", "pass1_segments",
+        "pass1_blocks", "pass2_segments", "pass2_blocks", "scalar_segments", "pass1_chunk",
+        "pass2_chunk", "table_bytes")]
+
+    def as_dict(self) -> dict:
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+class PlanSegment(ctypes.Structure):
+    _fields_ = [("tensor", ctypes.c_int64), ("offset", ctypes.c_int64),
+                ("numel", ctypes.c_int64), ("nvec", ctypes.c_int64),
+                ("head", ctypes.c_int32), ("tail", ctypes.c_int32),
+                ("vec_elems", ctypes.c_int32), ("block", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_PP = ctypes.POINTER(ctypes.c_void_p)
+# name -> (restype, argtypes); mirrors include/somaopt.h
+SIGNATURES = {
+    "somaopt_init_tensor_table": (ctypes.c_int, [ctypes.POINTER(TensorDesc), ctypes.c_int64,
+                                                 ctypes.POINTER(Group), ctypes.c_int32,
+                                                 ctypes.c_double, ctypes.c_double, ctypes.c_int64,
+                                                 _P, _PP]),
+    "somaopt_grad_sqnorm": (ctypes.c_int, [_P, _P]),
+    "somaopt_fused_adamw_step": (ctypes.c_int, [_P, _P]),
+    "somaopt_set_groups": (ctypes.c_int, [_P, ctypes.POINTER(Group), ctypes.c_int32, _P]),
+    "somaopt_set_clip": (ctypes.c_int, [_P, ctypes.c_double, ctypes.c_double, _P]),
+    "somaopt_set_step": (ctypes.c_int, [_P, ctypes.c_int64, _P]),
+    "somaopt_capture_step": (ctypes.c_int, [_P]),
+    "somaopt_replay_step": (ctypes.c_int, [_P, _P]),
+    "somaopt_device_stats": (ctypes.c_int, [_P, _PP]),
+    "somaopt_read_stats": (ctypes.c_int, [_P, ctypes.POINTER(Stats),
+                                          ctypes.POINTER(ctypes.c_int64), _P]),
+    "somaopt_get_plan_info": (ctypes.c_int, [_P, ctypes.POINTER(PlanInfo)]),
+    "somaopt_debug_plan": (ctypes.c_int64, [ctypes.POINTER(TensorDesc), ctypes.c_int64,
+                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                            ctypes.c_int64, ctypes.POINTER(PlanSegment),
+                                            ctypes.c_int64, ctypes.POINTER(PlanInfo)]),
+    "somaopt_destroy": (None, [_P]),
+    "somaopt_last_error": (ctypes.c_char_p, []),
+    "somaopt_version": (ctypes.c_char_p, []),
+}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class SomaoptError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{_STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libsomaopt.so (built in-tree by ``tensor_optimizer_step_amd.build``)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m tensor_optimizer_step_amd.build`"
+                           " (the optimizer has no non-HIP fallback)")
+    try:
+        import torch  # noqa: F401  (share torch's HIP runtime when torch is present)
+    except ImportError:
+        pass
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load().somaopt_last_error().decode()
+
+
+def _check(rc: int) -> int:
+    if rc < 0:
+        raise SomaoptError(rc, last_error())
+    return rc
+
+
+def _stream_ptr(stream) -> Optional[int]:
+    """hipStream_t of a torch stream (or an int/None passed through)."""
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream or None
+    if isinstance(stream, int):
+        return stream or None
+    return stream.cuda_stream or None
+
+
+def make_groups(groups: Sequence) -> ctypes.Array:
+    """Accepts objects with lr/weight_decay/beta1/beta2/eps attributes or dicts."""
+    arr = (Group * len(groups))()
+    for k, g in enumerate(groups):
+        get = (lambda n: g[n]) if isinstance(g, dict) else (lambda n: getattr(g, n))
+        arr[k] = Group(float(get("lr")), float(get("weight_decay")), float(get("beta1")),
+                       float(get("beta2")), float(get("eps")))
+    return arr
+
+
+def make_descs(rows: Sequence[tuple]) -> ctypes.Array:
+    """rows: (param_ptr, grad_ptr, exp_avg_ptr, exp_avg_sq_ptr, numel, grad_dtype, group,
+    trainable, owner) with raw integer pointers."""
+    arr = (TensorDesc * max(len(rows), 1))()
+    for i, r in enumerate(rows):
+        arr[i] = TensorDesc(*(int(x) if x is not None else None for x in r[:4]),
+                            int(r[4]), int(r[5]), int(r[6]), int(r[7]), int(r[8]))
+    return arr
+
+
+def torch_grad_dtype(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported gradient dtype {t.dtype}")
+
+
+def debug_plan(rows: Sequence[tuple], n_groups: int, pass_: int, pass1_chunk: int = 0,
+               pass2_chunk: int = 0):
+    """Host-only plan of one pass; returns (list of PlanSegment, PlanInfo)."""
+    lib = load()
+    descs = make_descs(rows)
+    info = PlanInfo()
+    n = _check(lib.somaopt_debug_plan(descs, len(rows), n_groups, pass_, pass1_chunk,
+                                      pass2_chunk, None, 0, ctypes.byref(info)))
+    segs = (PlanSegment * max(n, 1))()
+    _check(lib.somaopt_debug_plan(descs, len(rows), n_groups, pass_, pass1_chunk, pass2_chunk,
+                                  segs, n, ctypes.byref(info)))
+    return list(segs)[:n], info
+
+
+class FusedAdamW:
+    """One somaopt handle over a table of tensors.
+
+    ``params``, ``exp_avgs``, ``exp_avg_sqs`` are fp32 CUDA tensors and
+    ``grads`` fp32 or bf16 CUDA tensors (entries of frozen tensors may be
+    None).  The tensors must stay alive and in place while the handle lives.
+    """
+
+    def __init__(self, params: Sequence, grads: Sequence, exp_avgs: Sequence,
+                 exp_avg_sqs: Sequence, group_of: Sequence[int], groups: Sequence,
+                 max_norm: float, grad_divisor: float, trainable: Optional[Sequence[bool]] = None,
+                 owner: Optional[Sequence[bool]] = None, initial_step: int = 0, stream=None):
+        self._lib = load()
+        n = len(params)
+        trainable = [True] * n if trainable is None else list(trainable)
+        owner = [True] * n if owner is None else list(owner)
+        rows = []
+        self._keep = []   # references that keep the tensors alive
+        for i in range(n):
+            p, g, m, v = params[i], grads[i], exp_avgs[i], exp_avg_sqs[i]
+            if not trainable[i]:
+                rows.append((0, 0, 0, 0, 0 if p is None else p.numel(), F32, int(group_of[i]), 0,
+                             int(bool(owner[i]))))
+                continue
+            rows.append((p.data_ptr(), g.data_ptr(), m.data_ptr(), v.data_ptr(), p.numel(),
+                         torch_grad_dtype(g), int(group_of[i]), 1, int(bool(owner[i]))))
+            self._keep.append((p, g, m, v))
+        self.n_groups = len(groups)
+        self._groups = make_groups(groups)
+        descs = make_descs(rows)
+        h = ctypes.c_void_p()
+        _check(self._lib.somaopt_init_tensor_table(
+            descs, n, self._groups, self.n_groups, float(max_norm), float(grad_divisor),
+            int(initial_step), _stream_ptr(stream), ctypes.byref(h)))
+        self._h = h
+
+    # -- step path ---------------------------------------------------------
+    def grad_sqnorm(self, stream=None) -> None:
+        _check(self._lib.somaopt_grad_sqnorm(self._h, _stream_ptr(stream)))
+
+    def fused_adamw_step(self, stream=None) -> None:
+        _check(self._lib.somaopt_fused_adamw_step(self._h, _stream_ptr(stream)))
+
+    def step(self, stream=None) -> None:
+        """Eager step: norm pass, then update pass."""
+        self.grad_sqnorm(stream)
+        self.fused_adamw_step(stream)
+
+    def capture(self) -> None:
+        _check(self._lib.somaopt_capture_step(self._h))
+
+    def replay(self, stream=None) -> None:
+        _check(self._lib.somaopt_replay_step(self._h, _stream_ptr(stream)))
+
+    # -- settings ----------------------------------------------------------
+    def set_groups(self, groups: Sequence, stream=None) -> None:
+        self._groups = make_groups(groups)
+        _check(self._lib.somaopt_set_groups(self._h, self._groups, len(groups), _stream_ptr(stream)))
+
+    def set_lrs(self, lrs: Sequence[float], stream=None) -> None:
+        """Change only the groups' learning rates (a schedule step)."""
+        g = self._groups
+        for k, lr in enumerate(lrs):
+            g[k].lr = float(lr)
+        _check(self._lib.somaopt_set_groups(self._h, g, self.n_groups, _stream_ptr(stream)))
+
+    def set_clip(self, max_norm: float, grad_divisor: float, stream=None) -> None:
+        _check(self._lib.somaopt_set_clip(self._h, float(max_norm), float(grad_divisor),
+                                          _stream_ptr(stream)))
+
+    def set_step(self, step: int, stream=None) -> None:
+        _check(self._lib.somaopt_set_step(self._h, int(step), _stream_ptr(stream)))
+
+    # -- inspection --------------------------------------------------------
+    def read_stats(self, stream=None):
+        st = Stats()
+        steps = (ctypes.c_int64 * self.n_groups)()
+        _check(self._lib.somaopt_read_stats(self._h, ctypes.byref(st), steps, _stream_ptr(stream)))
+        return st, list(steps)
+
+    def device_stats_ptr(self) -> int:
+        p = ctypes.c_void_p()
+        _check(self._lib.somaopt_device_stats(self._h, ctypes.byref(p)))
+        return p.value
+
+    def plan_info(self) -> PlanInfo:
+        info = PlanInfo()
+        _check(self._lib.somaopt_get_plan_info(self._h, ctypes.byref(info)))
+        return info
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            self._lib.somaopt_destroy(self._h)
+            self._h = None
+            self._keep = []
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def version() -> str:
+    return load().somaopt_version().decode()

@@ -1,0 +1,345 @@
+"""GPU parity of the HIP path (through the C-ABI) against the fp64 oracle.
+
+Inputs are seeded and synthetic (tensor_optimizer_step_amd.workloads), created
+on the GPU with torch's generator and copied to the host for the oracle.
+Sizes here finish in seconds on the oracle yet span many workgroups and ragged
+tails; full-size workloads are in test_gpu_fullsize.py.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from tensor_optimizer_step_amd import workloads as W
+
+from parity_util import (assert_close, assert_norm, allocate, fill_grads, host, log,
+                         make_handle, make_oracle)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from tensor_optimizer_step_amd import somaopt
+    somaopt.load()          # fail loudly if the library is missing
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def run_and_compare(wl, steps=None, graph=True, max_norm=None, divisor=None, check_every_step=True):
+    """Run ``steps`` updates on the GPU and the oracle; compare everything."""
+    steps = wl.steps if steps is None else steps
+    log(f"[parity] {wl.name}: {wl.n_tensors} tensors, {wl.trainable_numel} trainable, "
+        f"{steps} steps, graph={graph}")
+    st = allocate(wl)
+    p0 = [host(x) for x in st.p]
+    frozen_before = {i: (host(st.p[i]), host(st.m[i]), host(st.v[i]))
+                     for i, t in enumerate(wl.tensors) if not t.trainable}
+    kw = {}
+    if max_norm is not None:
+        kw["max_norm"] = max_norm
+    if divisor is not None:
+        kw["grad_divisor"] = divisor
+    opt = make_handle(wl, st, **kw)
+    ora = make_oracle(wl, p0, max_norm=max_norm, divisor=divisor)
+    if graph:
+        opt.capture()
+    for k in range(1, steps + 1):
+        fill_grads(wl, st, k)
+        grads = [host(g) for g in st.g]
+        lrs = wl.lrs_for_step(k)
+        opt.set_lrs(lrs)
+        if graph:
+            opt.replay()
+        else:
+            opt.step()
+        stats, t = opt.read_stats()
+        want = ora.step(grads, lrs)
+        if check_every_step or k == steps:
+            assert_norm(stats.norm, want.norm)
+            assert stats.clip_coef == pytest.approx(want.coef, rel=1e-12)
+            assert stats.nonfinite == 0
+            assert t == [k] * len(wl.groups)
+        # gradient buffers are never written
+        for i, g in enumerate(st.g):
+            assert np.array_equal(host(g).view(np.uint8), grads[i].view(np.uint8)), f"grad {i} changed"
+    torch.cuda.synchronize()
+    worst = {"p": 0.0, "m": 0.0, "v": 0.0}
+    for i, t in enumerate(wl.tensors):
+        if not t.trainable:
+            fb = frozen_before[i]
+            for name, a, b in zip("pmv", (st.p[i], st.m[i], st.v[i]), fb):
+                assert np.array_equal(host(a).view(np.uint32), b.view(np.uint32)), f"frozen {name}{i}"
+            continue
+        worst["p"] = max(worst["p"], assert_close(f"p[{i}]", host(st.p[i]), ora.p[i]))
+        worst["m"] = max(worst["m"], assert_close(f"m[{i}]", host(st.m[i]), ora.m[i]))
+        worst["v"] = max(worst["v"], assert_close(f"v[{i}]", host(st.v[i]), ora.v[i]))
+    log(f"[parity] {wl.name}: max rel err p={worst['p']:.2e} m={worst['m']:.2e} v={worst['v']:.2e}")
+    opt.close()
+    return st, ora
+
+
+def test_tiny_one_step_eager():
+    run_and_compare(W.tiny(), graph=False)
+
+
+def test_tiny_one_step_graph():
+    run_and_compare(W.tiny(seed_offset=1), graph=True)
+
+
+def test_tiny_micro_batch_divisor():
+    # the veRL page's accumulation divisor: 128 // 8 = 16 micro-batches
+    run_and_compare(W.tiny(seed_offset=2), steps=3, divisor=16.0)
+
+
+def test_action_expert_scaled_bf16_ten_steps():
+    wl = W.action_expert(blocks=2, d=256, mlp=1024, action_dim=32)
+    run_and_compare(wl)
+
+
+def test_launch_bound_full_ten_steps():
+    # 20,000 tensors, 6,000 frozen with NaN gradients, warm-up schedule, 3 groups
+    run_and_compare(W.launch_bound(), check_every_step=True)
+
+
+def test_launch_bound_clipped_variant():
+    run_and_compare(W.launch_bound(n_tensors=3000), steps=4, max_norm=1.0)
+
+
+def test_edge_sizes_and_empty_tensors():
+    tensors = [W.TensorSpec(f"e{i}", n, i % 2, W.F32 if i % 3 else W.BF16)
+               for i, n in enumerate([0, 1, 2, 3, 4, 5, 7, 8, 9, 255, 256, 257, 1023, 4095,
+                                      8191, 8192, 8193, 0, 32767, 32768, 32769, 65537])]
+    wl = W.Workload("edges", 1, tensors, [W.GroupHP(1e-3, 0.1), W.GroupHP(2e-3, 0.0)],
+                    max_norm=1.0, grad_divisor=2.0, steps=3)
+    run_and_compare(wl)
+
+
+def test_no_owned_or_trainable_tensors():
+    tensors = [W.TensorSpec(f"f{i}", 100, 0, W.F32, trainable=False) for i in range(3)]
+    wl = W.Workload("all_frozen", 1, tensors, [W.GroupHP(1e-3, 0.1)], 1.0, 1.0, steps=2,
+                    nan_frozen_grads=True)
+    run_and_compare(wl)
+
+
+def _arena_case(seed):
+    """Tensors packed into shared arenas at odd element offsets, canaries in between.
+
+    Half the tensors share one offset modulo 4 across p/m/v/g (vector path with
+    a scalar head); the rest differ (scalar fallback).
+    """
+    rng = np.random.default_rng(seed)
+    wl = W.tiny(seed_offset=seed, n_tensors=24, max_numel=9000)
+    n = wl.n_tensors
+    CANARY = 0x7FA5A5A5         # a NaN payload no computation produces
+    offs = {k: [] for k in "pmvg"}
+    pos = {k: 3 for k in "pmvg"}
+    for i, t in enumerate(wl.tensors):
+        common = int(rng.integers(0, 4))
+        for k in "pmvg":
+            sh = common if i % 2 == 0 else int(rng.integers(0, 4))
+            pos[k] += 5 + sh
+            offs[k].append(pos[k])
+            pos[k] += t.numel
+    arenas = {k: torch.full((pos[k] + 11,), 0, dtype=torch.int32, device="cuda").fill_(CANARY)
+              .view(torch.float32) for k in "pmvg"}
+    return wl, offs, arenas, CANARY
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_arena_odd_offsets_and_canaries(seed):
+    from parity_util import DeviceState
+    wl, offs, ar, canary = _arena_case(seed)
+    log(f"[parity] arena seed={seed}")
+    st = DeviceState([], [], [], [])
+    for i, t in enumerate(wl.tensors):
+        n = t.numel
+        st.p.append(ar["p"][offs["p"][i]:offs["p"][i] + n])
+        st.m.append(ar["m"][offs["m"][i]:offs["m"][i] + n])
+        st.v.append(ar["v"][offs["v"][i]:offs["v"][i] + n])
+        st.g.append(ar["g"][offs["g"][i]:offs["g"][i] + n])
+        st.p[i].copy_(W.param_values(wl, i, "cuda"))
+        st.m[i].zero_()
+        st.v[i].zero_()
+    masks = {}
+    for k in "pmvg":
+        msk = torch.ones(ar[k].numel(), dtype=torch.bool)
+        for i, t in enumerate(wl.tensors):
+            msk[offs[k][i]:offs[k][i] + t.numel] = False
+        masks[k] = msk.numpy()
+    p0 = [host(x) for x in st.p]
+    opt = make_handle(wl, st)
+    info = opt.plan_info()
+    assert info.scalar_segments > 0       # both paths are exercised
+    ora = make_oracle(wl, p0)
+    for k in range(1, 3):
+        fill_grads(wl, st, k)
+        grads = [host(g) for g in st.g]
+        opt.step()
+        stats, _ = opt.read_stats()
+        want = ora.step(grads)
+        assert_norm(stats.norm, want.norm)
+    for i in range(wl.n_tensors):
+        assert_close(f"p[{i}]", host(st.p[i]), ora.p[i])
+        assert_close(f"m[{i}]", host(st.m[i]), ora.m[i])
+        assert_close(f"v[{i}]", host(st.v[i]), ora.v[i])
+    for k in "pmvg":
+        words = ar[k].view(torch.int32).cpu().numpy()
+        assert (words[masks[k]] == canary).all(), f"canary overwritten in arena {k}"
+    opt.close()
+
+
+def _bits(st):
+    return [host(x).view(np.uint32).copy() for x in st.p + st.m + st.v]
+
+
+def _run_steps(wl, steps, graph, scale_pow2=0):
+    st = allocate(wl)
+    opt = make_handle(wl, st, grad_divisor=wl.grad_divisor * 2.0 ** scale_pow2)
+    if graph:
+        opt.capture()
+    norms = []
+    for k in range(1, steps + 1):
+        fill_grads(wl, st, k)
+        if scale_pow2:
+            for g in st.g:
+                g.mul_(2.0 ** scale_pow2)        # exact for a power of two
+        opt.set_lrs(wl.lrs_for_step(k))
+        opt.replay() if graph else opt.step()
+        s, _ = opt.read_stats()
+        norms.append((s.norm, s.clip_coef))
+    torch.cuda.synchronize()
+    out = _bits(st)
+    opt.close()
+    return out, norms
+
+
+def test_graph_replay_equals_eager_bitwise():
+    wl = W.launch_bound(n_tensors=2000)
+    a, na = _run_steps(wl, 4, graph=False)
+    b, nb = _run_steps(wl, 4, graph=True)
+    assert na == nb
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
+
+
+def test_run_to_run_bitwise_determinism():
+    wl = W.action_expert(blocks=1, d=512, mlp=2048)
+    a, na = _run_steps(wl, 3, graph=True)
+    b, nb = _run_steps(wl, 3, graph=True)
+    assert na == nb
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
+
+
+def test_power_of_two_metamorphic():
+    # scaling every gradient and the divisor by 2^j changes nothing, bit for bit
+    wl = W.tiny(seed_offset=3)
+    wl.steps = 2
+    a, na = _run_steps(wl, 2, graph=True)
+    b, nb = _run_steps(wl, 2, graph=True, scale_pow2=5)
+    assert [x[0] for x in na] == [x[0] for x in nb]
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
+
+
+def test_resume_equals_continuation():
+    wl = W.launch_bound(n_tensors=500)
+    full, _ = _run_steps(wl, 6, graph=False)
+    # 3 steps, then a fresh handle on the same state with initial_step=3
+    st = allocate(wl)
+    opt = make_handle(wl, st)
+    for k in range(1, 4):
+        fill_grads(wl, st, k)
+        opt.set_lrs(wl.lrs_for_step(k))
+        opt.step()
+    opt.close()
+    opt = make_handle(wl, st, initial_step=3)
+    for k in range(4, 7):
+        fill_grads(wl, st, k)
+        opt.set_lrs(wl.lrs_for_step(k))
+        opt.step()
+    _, t = opt.read_stats()
+    assert t == [6, 6, 6]
+    torch.cuda.synchronize()
+    assert all(np.array_equal(x, y) for x, y in zip(full, _bits(st)))
+    opt.close()
+
+
+def test_nonfinite_flag_and_remeasure():
+    wl = W.tiny(seed_offset=4)
+    st = allocate(wl)
+    opt = make_handle(wl, st)
+    fill_grads(wl, st, 1)
+    st.g[5][0] = float("inf")
+    opt.grad_sqnorm()
+    s, t = opt.read_stats()
+    assert s.nonfinite == 1 and s.clip_coef == 0.0 and t == [1]
+    # measuring again before the update does not advance the step
+    st.g[5][0] = 0.0
+    opt.grad_sqnorm()
+    s, t = opt.read_stats()
+    assert s.nonfinite == 0 and math.isfinite(s.norm) and t == [1]
+    opt.fused_adamw_step()
+    opt.close()
+
+
+def test_call_order_errors():
+    from tensor_optimizer_step_amd.somaopt import SomaoptError, E_STATE, E_INVALID
+    wl = W.tiny(seed_offset=5, n_tensors=4)
+    st = allocate(wl)
+    opt = make_handle(wl, st)
+    with pytest.raises(SomaoptError) as e:
+        opt.fused_adamw_step()
+    assert e.value.code == E_STATE
+    with pytest.raises(SomaoptError) as e:
+        opt.replay()
+    assert e.value.code == E_STATE          # not captured
+    opt.capture()
+    opt.grad_sqnorm()
+    with pytest.raises(SomaoptError) as e:
+        opt.replay()
+    assert e.value.code == E_STATE          # eager norm pass pending
+    opt.fused_adamw_step()
+    opt.replay()
+    with pytest.raises(SomaoptError) as e:
+        opt.set_groups([W.GroupHP(1e-3, 0.0, beta1=1.0)])
+    assert e.value.code == E_INVALID
+    with pytest.raises(SomaoptError):
+        opt.set_clip(0.0, 1.0)
+    opt.close()
+
+
+def test_rejects_host_memory_and_out_of_range():
+    from tensor_optimizer_step_amd.somaopt import SomaoptError
+    wl = W.tiny(seed_offset=6, n_tensors=2, max_numel=64)
+    st = allocate(wl)
+    bad = st.p[0].cpu()                      # host memory is never handed to a kernel
+    from parity_util import DeviceState
+    st2 = DeviceState([bad] + st.p[1:], st.g, st.m, st.v)
+    with pytest.raises(SomaoptError, match="device"):
+        make_handle(wl, st2)
+    # a buffer whose declared size runs past the end of its allocation is
+    # rejected before any kernel could touch it (64 MiB: its own allocation)
+    torch.cuda.empty_cache()
+    x = torch.zeros(1 << 24, device="cuda")
+    from tensor_optimizer_step_amd.somaopt import FusedAdamW
+    with pytest.raises(SomaoptError, match="past the end"):
+        FusedAdamW([_Fake(x[-50:], 100)], [x[200:300]], [x[0:100]], [x[100:200]], [0],
+                   wl.groups, 1.0, 1.0)
+
+
+class _Fake:
+    """A tensor stand-in that claims more elements than it has."""
+
+    def __init__(self, t, n):
+        self.t, self.n = t, n
+        self.dtype = t.dtype
+
+    def data_ptr(self):
+        return self.t.data_ptr()
+
+    def numel(self):
+        return self.n
