@@ -10,13 +10,15 @@ namespace somaopt {
 
 constexpr int kPass1Threads = 256;
 constexpr int kPass2Threads = 256;
+constexpr int kFinalizeThreads = 1024;
+// Update pass: 4-element vectors per thread per batch (see update_segment).
+constexpr int kVecsPerThread = 4;
 
 struct Pass1Args {
     const Seg1* segs;
     const uint32_t* blk_first;   // n_blocks + 1 entries
     uint32_t n_blocks;           // >= 1
     double* partials;            // n_blocks entries, one per workgroup
-    uint32_t* ticket;            // completion counter, 0 between launches
     DevState* state;
     int32_t n_groups;
     int32_t advance;             // 1: this pass opens a new update (t += 1)

@@ -16,7 +16,8 @@ Workloads (all synthetic; no dataset or trained weight is involved):
                     groups with a linear lr warm-up over ten steps.
 * ``backbone_7b``   a 32-layer d=4096 / MLP 11008 / vocab 32064 backbone
                     (6,738,939,904 elements), bf16 gradients whose global norm
-                    alternates between 0.5 and 5 times max_norm.
+                    alternates between 0.5 and 5 times max_norm (two seeded
+                    draws, scaled per step, repeating with period 2).
 * ``sharded_7b``    the backbone's matrices cut into four contiguous shards held
                     together on one device, with every RMSNorm replicated in each
                     shard and owned only by shard 0; cosine lr schedule.
@@ -88,6 +89,7 @@ class Workload:
     schedule: str = "constant"        # constant | warmup | cosine
     nan_frozen_grads: bool = False     # fill frozen tensors' grads with NaN
     norm_targets: Optional[Sequence[float]] = None  # per-step target global norm
+    grad_period: Optional[int] = None  # >0: gradient draws repeat with this period
     meta: dict = field(default_factory=dict)
 
     # ----------------------------------------------------------------- sizes
@@ -218,7 +220,7 @@ def backbone_7b(layers: int = 32, d: int = 4096, mlp: int = 11008, vocab: int = 
         config=4, tensors=_backbone_tensors(layers, d, mlp, vocab),
         groups=[GroupHP(lr=PAGE_LR, weight_decay=0.01), GroupHP(lr=PAGE_LR, weight_decay=0.0)],
         max_norm=PAGE_MAX_NORM, grad_divisor=1.0, steps=steps,
-        p_std=0.02, norm_targets=(0.5 * PAGE_MAX_NORM, 5.0 * PAGE_MAX_NORM),
+        p_std=0.02, norm_targets=(0.5 * PAGE_MAX_NORM, 5.0 * PAGE_MAX_NORM), grad_period=2,
         meta=dict(layers=layers, d=d, mlp=mlp, vocab=vocab))
 
 
@@ -335,7 +337,8 @@ def grad_values(wl: Workload, index: int, step: int, device="cpu"):
     dt = torch.bfloat16 if spec.grad_dtype == BF16 else torch.float32
     if not spec.trainable and wl.nan_frozen_grads:
         return torch.full((spec.numel,), float("nan"), dtype=dt, device=device)
-    x = torch.randn(spec.numel, generator=_gen(wl.seed(SEED_GRADS, index, step), device),
+    draw = step if not wl.grad_period else 1 + (step - 1) % wl.grad_period
+    x = torch.randn(spec.numel, generator=_gen(wl.seed(SEED_GRADS, index, draw), device),
                     device=device, dtype=torch.float32)
     x.mul_(wl.grad_std(step))
     return x.to(dt)

@@ -3,7 +3,7 @@
 Inputs are seeded and synthetic (tensor_optimizer_step_amd.workloads), created
 on the GPU with torch's generator and copied to the host for the oracle.
 Sizes here finish in seconds on the oracle yet span many workgroups and ragged
-tails; full-size workloads are in test_gpu_fullsize.py.
+tails; full-size workloads are in test_gpu_parity_fullsize.py.
 """
 import math
 
