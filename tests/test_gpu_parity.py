@@ -79,7 +79,7 @@ def run_and_compare(wl, steps=None, graph=True, max_norm=None, divisor=None, che
         worst["p"] = max(worst["p"], assert_close(f"p[{i}]", host(st.p[i]), ora.p[i]))
         worst["m"] = max(worst["m"], assert_close(f"m[{i}]", host(st.m[i]), ora.m[i]))
         worst["v"] = max(worst["v"], assert_close(f"v[{i}]", host(st.v[i]), ora.v[i]))
-    log(f"[parity] {wl.name}: max rel err p={worst['p']:.2e} m={worst['m']:.2e} v={worst['v']:.2e}")
+    log(f"[parity] {wl.name}: tensor-wise rel err p={worst['p']:.2e} m={worst['m']:.2e} v={worst['v']:.2e}")
     opt.close()
     return st, ora
 

@@ -144,7 +144,7 @@ def run_unsharded(wl):
     for i in range(wl.n_tensors):
         for j, (dev_t, want) in enumerate(((p[i], ora.p[i]), (m[i], ora.m[i]), (v[i], ora.v[i]))):
             worst[j] = max(worst[j], assert_close(f"{'pmv'[j]}[{i}]", _gather(dev_t, idx[i]).numpy(), want))
-    log(f"[fullsize] {wl.name}: max rel err p={worst[0]:.2e} m={worst[1]:.2e} v={worst[2]:.2e}")
+    log(f"[fullsize] {wl.name}: tensor-wise rel err p={worst[0]:.2e} m={worst[1]:.2e} v={worst[2]:.2e}")
     opt.close()
     del p, g, m, v
 
