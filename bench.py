@@ -41,6 +41,8 @@ def parse():
                     choices=["action_expert", "backbone_7b", "launch_bound", "tiny"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
+    ap.add_argument("--lowp", choices=["none", "bf16", "f16"], default="none",
+                    help="also write a low-precision working copy of the weights (+2 B/element)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for HBM counter scaling)")
     return ap.parse_args()
@@ -50,17 +52,18 @@ def kernel_hash() -> str:
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
 
-def bytes_per_step(wl) -> dict:
+def bytes_per_step(wl, lowp: bool = False) -> dict:
     """Algorithmic HBM bytes: norm pass reads g once; update pass reads g,p,m,v
-    and writes p,m,v (fp32 state, 2- or 4-byte gradient)."""
+    and writes p,m,v (fp32 state, 2- or 4-byte gradient), plus 2 bytes per
+    element for a low-precision working copy."""
     from tensor_optimizer_step_amd import workloads as W
     p1 = p2 = 0
     for t in wl.tensors:
         if not t.trainable:
             continue
-        gsz = 2 if t.grad_dtype == W.BF16 else 4
+        gsz = 4 if t.grad_dtype == W.F32 else 2
         p1 += gsz * t.numel
-        p2 += (gsz + 12 + 12) * t.numel
+        p2 += (gsz + 12 + 12 + (2 if lowp else 0)) * t.numel
     return {"pass1": p1, "pass2": p2, "total": p1 + p2}
 
 
@@ -157,12 +160,15 @@ def main():
         m.append(torch.zeros(t.numel, device=dev))
         v.append(torch.zeros(t.numel, device=dev))
     stream = torch.cuda.current_stream()
+    lowp = None
+    if args.lowp != "none":
+        lowp = [torch.empty(t.numel, dtype=W.torch_dtype(args.lowp), device=dev) for t in wl.tensors]
     opt = somaopt.FusedAdamW(p, g, m, v, [t.group for t in wl.tensors], wl.groups, wl.max_norm,
                              wl.grad_divisor, trainable=[t.trainable for t in wl.tensors],
-                             stream=stream)
+                             stream=stream, params_lowp=lowp)
     info = opt.plan_info()
     opt.capture()
-    bts = bytes_per_step(wl)
+    bts = bytes_per_step(wl, lowp is not None)
     n_elem = wl.trainable_numel
 
     # warm-up, then exactly K timed replays of the captured step
@@ -200,7 +206,7 @@ def main():
         raise RuntimeError("non-finite statistics in the benchmark run")
 
     p2_gbs = bts["pass2"] / (p2_ms * 1e-3) / 1e9
-    traffic = load_traffic(wl.name, bts["pass2"])
+    traffic = load_traffic(wl.name, bts["pass2"]) if lowp is None else None
     roofline = {"bound": "hbm", "achieved": round(p2_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(p2_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "adamw_pass2", "algorithmic_bytes_per_launch": bts["pass2"],
@@ -230,7 +236,7 @@ def main():
                    "grad_dtype": wl.tensors[0].grad_dtype, "state_dtype": "f32",
                    "model_bytes_per_step": bts["total"], "groups": len(wl.groups),
                    "pass1_blocks": info.pass1_blocks, "pass2_blocks": info.pass2_blocks,
-                   "graph": True},
+                   "graph": True, "working_copy": args.lowp},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

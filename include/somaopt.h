@@ -20,9 +20,10 @@
  *        p     = p - lr*wd*p - (lr / (1 - beta1^t)) * m / (sqrt(v / (1 - beta2^t)) + eps)
  *      with t the group's update count, 1 on the first update.
  * Gradient buffers are never written and frozen tensors are never read or
- * written (same paragraph).  bf16 gradients are widened to fp32 for the update
- * and the optimizer state stays fp32 (RLinf page, "Retaining Low-Precision
- * Gradients").
+ * written (same paragraph).  bf16 and fp16 gradients are widened to fp32 for
+ * the update, the optimizer state stays fp32, and an optional bf16/fp16
+ * working copy of the weights is rewritten from the fp32 master (RLinf page,
+ * "Retaining Low-Precision Gradients").
  *
  * Conventions for every call:
  *   - Pointers in somaopt_tensor_desc are DEVICE pointers on the device that
@@ -59,15 +60,18 @@ typedef enum {
 } somaopt_status;
 
 typedef enum {
-    SOMAOPT_F32 = 0,  /* IEEE binary32 gradient                                  */
-    SOMAOPT_BF16 = 1  /* bfloat16 gradient (top 16 bits of a binary32)           */
+    SOMAOPT_F32 = 0,  /* IEEE binary32                                            */
+    SOMAOPT_BF16 = 1, /* bfloat16 (top 16 bits of a binary32)                     */
+    SOMAOPT_F16 = 2   /* IEEE binary16                                            */
 } somaopt_dtype;
 
 /* One entry of the tensor table.  A tensor cut by a shard boundary, or a
  * replica, is simply another entry whose pointers address that piece. */
 typedef struct {
-    void* param;          /* fp32 weights, numel elements, updated in place    */
-    const void* grad;     /* gradient, grad_dtype, numel elements, read only   */
+    void* param;          /* fp32 weights (the master copy), numel elements,
+                             updated in place                                   */
+    const void* grad;     /* gradient, grad_dtype (any somaopt_dtype), numel
+                             elements, read only                                */
     void* exp_avg;        /* fp32 first moment m, updated in place             */
     void* exp_avg_sq;     /* fp32 second moment v, updated in place            */
     int64_t numel;        /* >= 0; 0 is allowed and skipped                    */
@@ -76,6 +80,14 @@ typedef struct {
     int32_t trainable;    /* 0: frozen; never read or written, pointers may be NULL */
     int32_t owner;        /* 1: counts in the global norm; 0: updated only (a
                              replica or a piece another rank owns)              */
+    void* param_lowp;     /* optional (NULL = none): bf16 or fp16 working copy
+                             of the weights, numel elements, overwritten by each
+                             update with the updated fp32 master rounded to
+                             nearest, ties to even (RLinf page, "Retaining
+                             Low-Precision Gradients": BF16/FP16 parameters keep
+                             an FP32 master copy)                               */
+    int32_t lowp_dtype;   /* SOMAOPT_BF16 or SOMAOPT_F16 when param_lowp is set */
+    int32_t reserved;     /* must be 0                                          */
 } somaopt_tensor_desc;
 
 /* Per-group hyperparameters (the group's lr at this step, after the caller's
@@ -146,9 +158,10 @@ typedef struct somaopt_handle somaopt_handle;
  *
  * Frozen descriptors are dropped here and never appear in any table.
  * Validation (SOMAOPT_E_INVALID): NULL pointer or misaligned (4-byte fp32,
- * 2-byte bf16) buffer on a trainable tensor, numel < 0, group out of range,
- * unknown dtype, owner/trainable not 0/1, any overlap between the p, m, v
- * buffers of trainable tensors or between a gradient and any p/m/v buffer,
+ * 2-byte bf16/fp16) buffer on a trainable tensor, numel < 0, group out of
+ * range, unknown dtype, owner/trainable not 0/1, a working copy whose dtype is
+ * not bf16/fp16, any overlap between the written buffers (p, m, v, working
+ * copy) of trainable tensors or between a gradient and any written buffer,
  * a buffer that is not device memory of the current device or that runs past
  * the end of its allocation (skipped if SOMAOPT_SKIP_POINTER_CHECK=1).
  * Tuning (optional environment): SOMAOPT_PASS1_CHUNK, SOMAOPT_PASS2_CHUNK =

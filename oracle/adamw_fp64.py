@@ -49,17 +49,39 @@ CLIP_EPS = 1e-6  # added to the norm in the clip coefficient (torch clip_grad_no
 def widen_grad(g: np.ndarray) -> np.ndarray:
     """Exact widening of a gradient buffer to float64.
 
-    ``g`` is either float32 values or uint16 bf16 bit patterns; bf16 is the top
-    half of an IEEE float32, so shifting the bits left by 16 is exact.  (RLinf
-    page, "Retaining Low-Precision Gradients": bf16 gradients are converted to
-    fp32 for the update.)
+    ``g`` is float32 values, float16 values, or uint16 bf16 bit patterns; bf16
+    is the top half of an IEEE float32, so shifting the bits left by 16 is
+    exact.  (RLinf page, "Retaining Low-Precision Gradients": gradients kept in
+    the compute dtype are converted to fp32 for the update.)
     """
     g = np.asarray(g)
     if g.dtype == np.uint16:
         return (g.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    if g.dtype == np.float32 or g.dtype == np.float64:
+    if g.dtype in (np.float16, np.float32, np.float64):
         return g.astype(np.float64)
     raise TypeError(f"unsupported gradient dtype {g.dtype}")
+
+
+def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """bf16 working copy of fp32 master weights: round to nearest, ties to even.
+
+    RLinf page, "Retaining Low-Precision Gradients": bf16/fp16 parameters keep
+    an fp32 master copy; the working copy is the master rounded to bf16.  The
+    rounding decision is taken from the fp32 value, as the master is fp32.
+    Returns uint16 bit patterns; NaN maps to a quiet NaN.
+    """
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    keep_lsb = (u >> 16) & 1
+    rounded = ((u + 0x7FFF + keep_lsb) >> 16).astype(np.uint16)
+    nan = np.isnan(np.asarray(x, dtype=np.float32))
+    return np.where(nan, np.uint16(0x7FC0), rounded)
+
+
+def round_to_f16(x: np.ndarray) -> np.ndarray:
+    """fp16 working copy of fp32 master weights (IEEE round to nearest even;
+    values beyond the fp16 range become infinities)."""
+    with np.errstate(over="ignore"):
+        return np.asarray(x, dtype=np.float32).astype(np.float16)
 
 
 def normalized_sumsq(grads: Sequence[np.ndarray], owned: Sequence[bool], divisor: float) -> float:

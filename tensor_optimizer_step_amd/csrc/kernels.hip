@@ -54,9 +54,35 @@ __device__ __forceinline__ T cload(const AS_CONST T* p) {
 #endif
 }
 
+// Exact widening of 16-bit gradients: bf16 is the top half of a binary32;
+// binary16 converts exactly with the hardware conversion.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float bf16_one(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+__device__ __forceinline__ float f16_one(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
+template <int DT>
+__device__ __forceinline__ float widen16(uint16_t h) {
+    if constexpr (DT == SOMAOPT_BF16) return bf16_one(h);
+    else return f16_one(h);
+}
+template <int DT>
+__device__ __forceinline__ float widen_lo(uint32_t w) {
+    if constexpr (DT == SOMAOPT_BF16) return bf16_lo(w);
+    else return f16_one((uint16_t)(w & 0xffffu));
+}
+template <int DT>
+__device__ __forceinline__ float widen_hi(uint32_t w) {
+    if constexpr (DT == SOMAOPT_BF16) return bf16_hi(w);
+    else return f16_one((uint16_t)(w >> 16));
+}
+
+// Working copy of an fp32 master weight: round to nearest, ties to even.
+template <int DT>
+__device__ __forceinline__ uint16_t narrow16(float x) {
+    if constexpr (DT == SOMAOPT_BF16) return __builtin_bit_cast(uint16_t, (__bf16)x);
+    else return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
 
 // ---------------------------------------------------------------- reductions
 
@@ -110,32 +136,39 @@ __device__ __forceinline__ double block_sum(double x, double* lds) {
 
 // ------------------------------------------------------------------ pass 1
 
+// Sum of squares of one 16-bit-gradient segment (bf16 or fp16): 16-byte loads
+// of eight values, exact widening, fp64 accumulation.
+template <int BS, int DT>
+__device__ __forceinline__ void sumsq16(const Seg1& sg, int tid, double& a0, double& a1) {
+    const AS_GLOBAL uint16_t* g = gptr<uint16_t>(sg.g);
+    for (uint32_t k = tid; k < sg.head; k += BS) {
+        const double x = widen16<DT>(g[k]);
+        a0 = fma(x, x, a0);
+    }
+    const AS_GLOBAL u32x4* gv = (const AS_GLOBAL u32x4*)(g + sg.head);
+#pragma unroll 2
+    for (uint32_t i = tid; i < sg.nvec; i += BS) {
+        const u32x4 q = gv[i];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const double lo = widen_lo<DT>(q[k]);
+            const double hi = widen_hi<DT>(q[k]);
+            a0 = fma(lo, lo, a0);
+            a1 = fma(hi, hi, a1);
+        }
+    }
+    if ((uint32_t)tid < sg.tail) {
+        const double x = widen16<DT>(g[sg.head + 8 * (size_t)sg.nvec + tid]);
+        a1 = fma(x, x, a1);
+    }
+}
+
 template <int BS>
 __device__ __forceinline__ void segment_sumsq(const Seg1& sg, int tid, double& a0, double& a1) {
     if (sg.dtype == SOMAOPT_BF16) {
-        const AS_GLOBAL uint16_t* g = gptr<uint16_t>(sg.g);
-        for (uint32_t k = tid; k < sg.head; k += BS) {
-            const double x = bf16_one(g[k]);
-            a0 = fma(x, x, a0);
-        }
-        const AS_GLOBAL u32x4* gv = (const AS_GLOBAL u32x4*)(g + sg.head);
-#pragma unroll 2
-        for (uint32_t i = tid; i < sg.nvec; i += BS) {
-            const u32x4 q = gv[i];
-            double x;
-            x = bf16_lo(q.x); a0 = fma(x, x, a0);
-            x = bf16_hi(q.x); a1 = fma(x, x, a1);
-            x = bf16_lo(q.y); a0 = fma(x, x, a0);
-            x = bf16_hi(q.y); a1 = fma(x, x, a1);
-            x = bf16_lo(q.z); a0 = fma(x, x, a0);
-            x = bf16_hi(q.z); a1 = fma(x, x, a1);
-            x = bf16_lo(q.w); a0 = fma(x, x, a0);
-            x = bf16_hi(q.w); a1 = fma(x, x, a1);
-        }
-        if ((uint32_t)tid < sg.tail) {
-            const double x = bf16_one(g[sg.head + 8 * (size_t)sg.nvec + tid]);
-            a1 = fma(x, x, a1);
-        }
+        sumsq16<BS, SOMAOPT_BF16>(sg, tid, a0, a1);
+    } else if (sg.dtype == SOMAOPT_F16) {
+        sumsq16<BS, SOMAOPT_F16>(sg, tid, a0, a1);
     } else {
         const AS_GLOBAL float* g = gptr<float>(sg.g);
         for (uint32_t k = tid; k < sg.head; k += BS) {
@@ -272,13 +305,10 @@ __device__ __forceinline__ void adamw_vec(f32x4& p, f32x4& m, f32x4& v, const f3
     }
 }
 
-template <bool BF16>
+template <int GDT>
 __device__ __forceinline__ float load_g1(const AS_GLOBAL char* gbase, size_t i) {
-    if constexpr (BF16) {
-        return bf16_one(((const AS_GLOBAL uint16_t*)gbase)[i]);
-    } else {
-        return ((const AS_GLOBAL float*)gbase)[i];
-    }
+    if constexpr (GDT == SOMAOPT_F32) return ((const AS_GLOBAL float*)gbase)[i];
+    else return widen16<GDT>(((const AS_GLOBAL uint16_t*)gbase)[i]);
 }
 
 // Streaming loads and stores carry the nontemporal hint: every byte is used
@@ -293,45 +323,59 @@ __device__ __forceinline__ void st_nt(AS_GLOBAL T* p, const T& v) {
     __builtin_nontemporal_store(v, p);
 }
 
-template <bool BF16>
+template <int GDT>
 __device__ __forceinline__ f32x4 widen_g4(const AS_GLOBAL char* gbase, uint32_t i) {
-    if constexpr (BF16) {
+    if constexpr (GDT == SOMAOPT_F32) {
+        return ld_nt((const AS_GLOBAL f32x4*)gbase + i);
+    } else {
         const u32x2 w = ld_nt((const AS_GLOBAL u32x2*)gbase + i);
         f32x4 r;
-        r.x = bf16_lo(w.x);
-        r.y = bf16_hi(w.x);
-        r.z = bf16_lo(w.y);
-        r.w = bf16_hi(w.y);
+        r.x = widen_lo<GDT>(w.x);
+        r.y = widen_hi<GDT>(w.x);
+        r.z = widen_lo<GDT>(w.y);
+        r.w = widen_hi<GDT>(w.y);
         return r;
-    } else {
-        return ld_nt((const AS_GLOBAL f32x4*)gbase + i);
     }
 }
+
+template <int LDT>
+__device__ __forceinline__ u32x2 narrow4(const f32x4& p) {
+    u32x2 r;
+    r.x = (uint32_t)narrow16<LDT>(p.x) | ((uint32_t)narrow16<LDT>(p.y) << 16);
+    r.y = (uint32_t)narrow16<LDT>(p.z) | ((uint32_t)narrow16<LDT>(p.w) << 16);
+    return r;
+}
+
+constexpr int kNoLowp = -1;
 
 // One segment of the update pass.  Each thread takes kVecsPerThread vectors
 // spaced BS apart and issues all of their loads before any arithmetic, so a
 // wave keeps 4 x (3 x 16 + 8 or 16) bytes per lane in flight; a segment of at
-// most BS * kVecsPerThread vectors is a single batch.
-template <int BS, bool BF16>
+// most BS * kVecsPerThread vectors is a single batch.  GDT is the gradient
+// dtype, LDT the working-copy dtype (kNoLowp: none).
+template <int BS, int GDT, int LDT>
 __device__ __forceinline__ void update_segment(const Seg2& sg, const GroupConst& c, float scale, int tid) {
     constexpr int U = kVecsPerThread;
-    constexpr size_t kGsz = BF16 ? 2 : 4;
+    constexpr size_t kGsz = GDT == SOMAOPT_F32 ? 4 : 2;
     AS_GLOBAL float* p = gptr<float>(sg.p);
     AS_GLOBAL float* m = gptr<float>(sg.m);
     AS_GLOBAL float* v = gptr<float>(sg.v);
     const AS_GLOBAL char* gb = gptr<char>(sg.g);
+    AS_GLOBAL uint16_t* lp = gptr<uint16_t>(sg.lowp);
     // Scalar head: a few elements before the first aligned vector, or the
-    // whole segment when p, m, v and g share no 16-byte alignment.
+    // whole segment when p, m, v, g (and the working copy) share no alignment.
     for (uint32_t k = tid; k < sg.head; k += BS) {
         float pp = p[k], mm = m[k], vq = v[k];
-        adamw_elem(pp, mm, vq, load_g1<BF16>(gb, k), c, scale);
+        adamw_elem(pp, mm, vq, load_g1<GDT>(gb, k), c, scale);
         p[k] = pp;
         m[k] = mm;
         v[k] = vq;
+        if constexpr (LDT != kNoLowp) lp[k] = narrow16<LDT>(pp);
     }
     AS_GLOBAL f32x4* pv = (AS_GLOBAL f32x4*)(p + sg.head);
     AS_GLOBAL f32x4* mv = (AS_GLOBAL f32x4*)(m + sg.head);
     AS_GLOBAL f32x4* vv = (AS_GLOBAL f32x4*)(v + sg.head);
+    AS_GLOBAL u32x2* lv = (AS_GLOBAL u32x2*)(lp + sg.head);
     const AS_GLOBAL char* gv = gb + sg.head * kGsz;
     const uint32_t nvec = sg.nvec;
     for (uint32_t i0 = tid; i0 < nvec; i0 += BS * U) {
@@ -343,7 +387,7 @@ __device__ __forceinline__ void update_segment(const Seg2& sg, const GroupConst&
                 pr[u] = ld_nt(pv + i);
                 mr[u] = ld_nt(mv + i);
                 vr[u] = ld_nt(vv + i);
-                gr[u] = widen_g4<BF16>(gv, i);
+                gr[u] = widen_g4<GDT>(gv, i);
             }
         }
 #pragma unroll
@@ -354,17 +398,29 @@ __device__ __forceinline__ void update_segment(const Seg2& sg, const GroupConst&
                 st_nt(pv + i, pr[u]);
                 st_nt(mv + i, mr[u]);
                 st_nt(vv + i, vr[u]);
+                if constexpr (LDT != kNoLowp) st_nt(lv + i, narrow4<LDT>(pr[u]));
             }
         }
     }
     if ((uint32_t)tid < sg.tail) {
         const size_t k = sg.head + 4 * (size_t)nvec + tid;
         float pp = p[k], mm = m[k], vq = v[k];
-        adamw_elem(pp, mm, vq, load_g1<BF16>(gb, k), c, scale);
+        adamw_elem(pp, mm, vq, load_g1<GDT>(gb, k), c, scale);
         p[k] = pp;
         m[k] = mm;
         v[k] = vq;
+        if constexpr (LDT != kNoLowp) lp[k] = narrow16<LDT>(pp);
     }
+}
+
+template <int BS, int GDT>
+__device__ __forceinline__ void update_segment_any(const Seg2& sg, const GroupConst& c, float scale, int tid) {
+    if (sg.lowp == nullptr)
+        update_segment<BS, GDT, kNoLowp>(sg, c, scale, tid);
+    else if (sg.lowp_dtype == SOMAOPT_BF16)
+        update_segment<BS, GDT, SOMAOPT_BF16>(sg, c, scale, tid);
+    else
+        update_segment<BS, GDT, SOMAOPT_F16>(sg, c, scale, tid);
 }
 
 template <int BS>
@@ -381,9 +437,11 @@ __global__ __launch_bounds__(BS) void adamw_pass2(Pass2Args a) {
         const Seg2 sg = cload(segs + s);
         const GroupConst c = cload(&st->gconst[sg.group]);
         if (sg.dtype == SOMAOPT_BF16)
-            update_segment<BS, true>(sg, c, scale, tid);
+            update_segment_any<BS, SOMAOPT_BF16>(sg, c, scale, tid);
+        else if (sg.dtype == SOMAOPT_F16)
+            update_segment_any<BS, SOMAOPT_F16>(sg, c, scale, tid);
         else
-            update_segment<BS, false>(sg, c, scale, tid);
+            update_segment_any<BS, SOMAOPT_F32>(sg, c, scale, tid);
     }
 }
 

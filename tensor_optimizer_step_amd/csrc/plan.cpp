@@ -12,10 +12,10 @@ namespace {
 struct Interval {
     uintptr_t lo, hi;   // [lo, hi)
     int64_t tensor;
-    int kind;           // 0 p, 1 m, 2 v, 3 g
+    int kind;           // 0 p, 1 m, 2 v, 3 g, 4 working copy
 };
 
-const char* kKindName[4] = {"param", "exp_avg", "exp_avg_sq", "grad"};
+const char* kKindName[5] = {"param", "exp_avg", "exp_avg_sq", "grad", "param_lowp"};
 
 std::string fmt(const char* f, long long a = 0, long long b = 0, long long c = 0) {
     char buf[256];
@@ -56,8 +56,16 @@ int validate_host(const somaopt_tensor_desc* d, int64_t n, int32_t n_groups, std
         }
         if (t.numel < 0) { err = fmt("tensor %lld: numel %lld < 0", i, t.numel); return SOMAOPT_E_INVALID; }
         if (t.numel > (int64_t(1) << 40)) { err = fmt("tensor %lld: numel too large", i); return SOMAOPT_E_INVALID; }
-        if (t.grad_dtype != SOMAOPT_F32 && t.grad_dtype != SOMAOPT_BF16) {
+        if (t.grad_dtype != SOMAOPT_F32 && t.grad_dtype != SOMAOPT_BF16 && t.grad_dtype != SOMAOPT_F16) {
             err = fmt("tensor %lld: unknown grad_dtype %lld", i, t.grad_dtype);
+            return SOMAOPT_E_INVALID;
+        }
+        if (t.param_lowp && t.lowp_dtype != SOMAOPT_BF16 && t.lowp_dtype != SOMAOPT_F16) {
+            err = fmt("tensor %lld: lowp_dtype %lld must be bf16 or fp16", i, t.lowp_dtype);
+            return SOMAOPT_E_INVALID;
+        }
+        if (t.reserved != 0) {
+            err = fmt("tensor %lld: reserved field must be 0", i);
             return SOMAOPT_E_INVALID;
         }
         if (t.group < 0 || t.group >= n_groups) {
@@ -68,9 +76,10 @@ int validate_host(const somaopt_tensor_desc* d, int64_t n, int32_t n_groups, std
         c.trainable_numel += t.numel;
         if (t.owner) c.owned_numel += t.numel;
         if (t.numel == 0) continue;
-        const void* ptrs[4] = {t.param, t.exp_avg, t.exp_avg_sq, t.grad};
-        const int64_t esz[4] = {4, 4, 4, grad_elem_bytes(t.grad_dtype)};
-        for (int k = 0; k < 4; ++k) {
+        const void* ptrs[5] = {t.param, t.exp_avg, t.exp_avg_sq, t.grad, t.param_lowp};
+        const int64_t esz[5] = {4, 4, 4, grad_elem_bytes(t.grad_dtype), 2};
+        const int nbuf = t.param_lowp ? 5 : 4;
+        for (int k = 0; k < nbuf; ++k) {
             uintptr_t a = reinterpret_cast<uintptr_t>(ptrs[k]);
             if (a == 0) {
                 err = std::string("tensor ") + std::to_string(i) + ": " + kKindName[k] + " pointer is NULL";
@@ -89,8 +98,9 @@ int validate_host(const somaopt_tensor_desc* d, int64_t n, int32_t n_groups, std
             iv.push_back(Interval{a, a + bytes, i, k});
         }
     }
-    // Overlap check: writable buffers (p, m, v) may overlap nothing; gradients
-    // may overlap other gradients (both read-only) but no p/m/v buffer.
+    // Overlap check: written buffers (p, m, v, working copy) may overlap
+    // nothing; gradients may overlap other gradients (both read only) but no
+    // written buffer.
     std::sort(iv.begin(), iv.end(), [](const Interval& x, const Interval& y) {
         return x.lo < y.lo || (x.lo == y.lo && x.hi < y.hi);
     });
@@ -155,10 +165,11 @@ Plan build_plan(const somaopt_tensor_desc* d, int64_t n, int pass, int64_t chunk
             head = common_head(a, s, 1, vec);
         } else {
             vec = 4;
-            uintptr_t a[4] = {reinterpret_cast<uintptr_t>(t.param), reinterpret_cast<uintptr_t>(t.exp_avg),
-                              reinterpret_cast<uintptr_t>(t.exp_avg_sq), reinterpret_cast<uintptr_t>(t.grad)};
-            int64_t s[4] = {4, 4, 4, gsz};
-            head = common_head(a, s, 4, vec);
+            uintptr_t a[5] = {reinterpret_cast<uintptr_t>(t.param), reinterpret_cast<uintptr_t>(t.exp_avg),
+                              reinterpret_cast<uintptr_t>(t.exp_avg_sq), reinterpret_cast<uintptr_t>(t.grad),
+                              reinterpret_cast<uintptr_t>(t.param_lowp)};
+            int64_t s[5] = {4, 4, 4, gsz, 2};
+            head = common_head(a, s, t.param_lowp ? 5 : 4, vec);
         }
         if (head < 0) {
             // No common alignment: the whole tensor takes the scalar path.

@@ -25,19 +25,22 @@ struct alignas(8) Seg1 {
 };
 static_assert(sizeof(Seg1) == 24, "Seg1 layout");
 
-// Device layout of an update-pass segment: the same run of p, m, v and g.
+// Device layout of an update-pass segment: the same run of p, m, v, g and the
+// optional low-precision working copy.
 struct alignas(16) Seg2 {
     float* p;
     float* m;
     float* v;
     const void* g;
+    void* lowp;         // bf16/fp16 working copy or NULL
     uint32_t head;      // scalar elements before the first 4-element vector
     uint32_t nvec;      // 4-element vectors (16 bytes of p/m/v, 8 or 16 of g)
     uint32_t tail;      // scalar elements after the last vector
     uint16_t group;
-    uint16_t dtype;
+    uint8_t dtype;      // gradient somaopt_dtype
+    uint8_t lowp_dtype; // working-copy somaopt_dtype (when lowp is set)
 };
-static_assert(sizeof(Seg2) == 48, "Seg2 layout");
+static_assert(sizeof(Seg2) == 64, "Seg2 layout");
 
 // Elements per workgroup.  Measured on MI355X: short workgroups (8192 gradient
 // elements in the norm pass, 4096 = 256 threads x 4 vectors x 4 elements in the
@@ -80,6 +83,6 @@ Plan build_plan(const somaopt_tensor_desc* d, int64_t n, int pass, int64_t chunk
 // Normalise a requested chunk: positive multiple of 8, at least 256 elements.
 int64_t normalise_chunk(int64_t requested, int64_t dflt);
 
-inline int64_t grad_elem_bytes(int32_t dtype) { return dtype == SOMAOPT_BF16 ? 2 : 4; }
+inline int64_t grad_elem_bytes(int32_t dtype) { return dtype == SOMAOPT_F32 ? 4 : 2; }
 
 }  // namespace somaopt

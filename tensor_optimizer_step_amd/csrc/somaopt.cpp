@@ -108,13 +108,14 @@ int64_t env_int(const char* name, int64_t dflt) {
 int check_pointers(const somaopt_tensor_desc* d, int64_t n, int dev) {
     const char* skip = std::getenv("SOMAOPT_SKIP_POINTER_CHECK");
     if (skip && std::strcmp(skip, "1") == 0) return SOMAOPT_OK;
-    static const char* kind[4] = {"param", "exp_avg", "exp_avg_sq", "grad"};
+    static const char* kind[5] = {"param", "exp_avg", "exp_avg_sq", "grad", "param_lowp"};
     for (int64_t i = 0; i < n; ++i) {
         const somaopt_tensor_desc& t = d[i];
         if (!t.trainable || t.numel == 0) continue;
-        const void* ptrs[4] = {t.param, t.exp_avg, t.exp_avg_sq, t.grad};
-        const size_t esz[4] = {4, 4, 4, (size_t)grad_elem_bytes(t.grad_dtype)};
-        for (int k = 0; k < 4; ++k) {
+        const void* ptrs[5] = {t.param, t.exp_avg, t.exp_avg_sq, t.grad, t.param_lowp};
+        const size_t esz[5] = {4, 4, 4, (size_t)grad_elem_bytes(t.grad_dtype), 2};
+        const int nbuf = t.param_lowp ? 5 : 4;
+        for (int k = 0; k < nbuf; ++k) {
             const std::string at = "tensor " + std::to_string(i) + " " + kind[k] + ": ";
             hipPointerAttribute_t attr;
             std::memset(&attr, 0, sizeof(attr));
@@ -292,11 +293,13 @@ int somaopt_init_tensor_table(const somaopt_tensor_desc* descs, int64_t n_tensor
         s2[i].m = static_cast<float*>(t.exp_avg) + s.offset;
         s2[i].v = static_cast<float*>(t.exp_avg_sq) + s.offset;
         s2[i].g = static_cast<const char*>(t.grad) + (size_t)s.offset * gsz;
+        s2[i].lowp = t.param_lowp ? static_cast<char*>(t.param_lowp) + (size_t)s.offset * 2 : nullptr;
         s2[i].head = (uint32_t)s.head;
         s2[i].nvec = (uint32_t)s.nvec;
         s2[i].tail = (uint32_t)s.tail;
         s2[i].group = (uint16_t)t.group;
-        s2[i].dtype = (uint16_t)t.grad_dtype;
+        s2[i].dtype = (uint8_t)t.grad_dtype;
+        s2[i].lowp_dtype = (uint8_t)(t.param_lowp ? t.lowp_dtype : 0);
     }
 
     DevState st;

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libsomaopt.so")
 
 F32 = 0
 BF16 = 1
+F16 = 2
 MAX_GROUPS = 64
 
 OK, E_INVALID, E_HIP, E_NOMEM, E_STATE = 0, -1, -2, -3, -4
@@ -28,7 +29,8 @@ class TensorDesc(ctypes.Structure):
                 ("exp_avg", ctypes.c_void_p), ("exp_avg_sq", ctypes.c_void_p),
                 ("numel", ctypes.c_int64), ("grad_dtype", ctypes.c_int32),
                 ("group", ctypes.c_int32), ("trainable", ctypes.c_int32),
-                ("owner", ctypes.c_int32)]
+                ("owner", ctypes.c_int32), ("param_lowp", ctypes.c_void_p),
+                ("lowp_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class Group(ctypes.Structure):
@@ -152,21 +154,27 @@ def make_groups(groups: Sequence) -> ctypes.Array:
 
 def make_descs(rows: Sequence[tuple]) -> ctypes.Array:
     """rows: (param_ptr, grad_ptr, exp_avg_ptr, exp_avg_sq_ptr, numel, grad_dtype, group,
-    trainable, owner) with raw integer pointers."""
+    trainable, owner[, param_lowp_ptr, lowp_dtype[, reserved]]) with raw integer pointers."""
     arr = (TensorDesc * max(len(rows), 1))()
     for i, r in enumerate(rows):
-        arr[i] = TensorDesc(*(int(x) if x is not None else None for x in r[:4]),
-                            int(r[4]), int(r[5]), int(r[6]), int(r[7]), int(r[8]))
+        ptrs = [int(x) if x else None for x in r[:4]]
+        lowp = int(r[9]) if len(r) > 9 and r[9] else None
+        ldt = int(r[10]) if len(r) > 10 else 0
+        rsv = int(r[11]) if len(r) > 11 else 0
+        arr[i] = TensorDesc(*ptrs, int(r[4]), int(r[5]), int(r[6]), int(r[7]), int(r[8]),
+                            lowp, ldt, rsv)
     return arr
 
 
-def torch_grad_dtype(t) -> int:
+def torch_dtype_code(t) -> int:
     import torch
-    if t.dtype == torch.bfloat16:
-        return BF16
-    if t.dtype == torch.float32:
-        return F32
-    raise TypeError(f"unsupported gradient dtype {t.dtype}")
+    codes = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+torch_grad_dtype = torch_dtype_code
 
 
 def debug_plan(rows: Sequence[tuple], n_groups: int, pass_: int, pass1_chunk: int = 0,
@@ -187,14 +195,17 @@ class FusedAdamW:
     """One somaopt handle over a table of tensors.
 
     ``params``, ``exp_avgs``, ``exp_avg_sqs`` are fp32 CUDA tensors and
-    ``grads`` fp32 or bf16 CUDA tensors (entries of frozen tensors may be
-    None).  The tensors must stay alive and in place while the handle lives.
+    ``grads`` fp32, bf16 or fp16 CUDA tensors (entries of frozen tensors may be
+    None).  ``params_lowp`` optionally gives a bf16/fp16 working copy per
+    tensor (None entries: no copy).  The tensors must stay alive and in place
+    while the handle lives.
     """
 
     def __init__(self, params: Sequence, grads: Sequence, exp_avgs: Sequence,
                  exp_avg_sqs: Sequence, group_of: Sequence[int], groups: Sequence,
                  max_norm: float, grad_divisor: float, trainable: Optional[Sequence[bool]] = None,
-                 owner: Optional[Sequence[bool]] = None, initial_step: int = 0, stream=None):
+                 owner: Optional[Sequence[bool]] = None, initial_step: int = 0, stream=None,
+                 params_lowp: Optional[Sequence] = None):
         self._lib = load()
         n = len(params)
         trainable = [True] * n if trainable is None else list(trainable)
@@ -207,9 +218,12 @@ class FusedAdamW:
                 rows.append((0, 0, 0, 0, 0 if p is None else p.numel(), F32, int(group_of[i]), 0,
                              int(bool(owner[i]))))
                 continue
+            lp = params_lowp[i] if params_lowp is not None else None
             rows.append((p.data_ptr(), g.data_ptr(), m.data_ptr(), v.data_ptr(), p.numel(),
-                         torch_grad_dtype(g), int(group_of[i]), 1, int(bool(owner[i]))))
-            self._keep.append((p, g, m, v))
+                         torch_dtype_code(g), int(group_of[i]), 1, int(bool(owner[i])),
+                         lp.data_ptr() if lp is not None else 0,
+                         torch_dtype_code(lp) if lp is not None else 0))
+            self._keep.append((p, g, m, v, lp))
         self.n_groups = len(groups)
         self._groups = make_groups(groups)
         descs = make_descs(rows)

@@ -39,6 +39,7 @@ import numpy as np
 
 F32 = "f32"
 BF16 = "bf16"
+F16 = "f16"
 
 # Purposes that enter the seed (seed = 1000 * config + purpose).
 SEED_SIZES = 1
@@ -334,7 +335,7 @@ def grad_values(wl: Workload, index: int, step: int, device="cpu"):
     """
     torch = _torch()
     spec = wl.tensors[index]
-    dt = torch.bfloat16 if spec.grad_dtype == BF16 else torch.float32
+    dt = torch_dtype(spec.grad_dtype)
     if not spec.trainable and wl.nan_frozen_grads:
         return torch.full((spec.numel,), float("nan"), dtype=dt, device=device)
     draw = step if not wl.grad_period else 1 + (step - 1) % wl.grad_period
@@ -344,6 +345,11 @@ def grad_values(wl: Workload, index: int, step: int, device="cpu"):
     return x.to(dt)
 
 
+def torch_dtype(name: str):
+    torch = _torch()
+    return {F32: torch.float32, BF16: torch.bfloat16, F16: torch.float16}[name]
+
+
 def bf16_bits(t) -> np.ndarray:
     """Raw uint16 bit patterns of a bf16 torch tensor (host copy)."""
     torch = _torch()
@@ -351,7 +357,7 @@ def bf16_bits(t) -> np.ndarray:
 
 
 def to_numpy_grad(t) -> np.ndarray:
-    """Host copy of a gradient: float32 array, or uint16 bf16 bit patterns."""
+    """Host copy of a gradient: float32/float16 array, or uint16 bf16 bit patterns."""
     torch = _torch()
     if t.dtype == torch.bfloat16:
         return bf16_bits(t)

@@ -46,8 +46,7 @@ def allocate(wl: W.Workload, device="cuda") -> DeviceState:
     p, g, m, v = [], [], [], []
     for i, t in enumerate(wl.tensors):
         p.append(W.param_values(wl, i, device))
-        dt = torch.bfloat16 if t.grad_dtype == W.BF16 else torch.float32
-        g.append(torch.empty(t.numel, dtype=dt, device=device))
+        g.append(torch.empty(t.numel, dtype=W.torch_dtype(t.grad_dtype), device=device))
         m.append(torch.zeros(t.numel, dtype=torch.float32, device=device))
         v.append(torch.zeros(t.numel, dtype=torch.float32, device=device))
     return DeviceState(p, g, m, v)

@@ -187,6 +187,38 @@ def test_validation_errors(bad, needle):
     assert needle in str(ei.value)
 
 
+def test_working_copy_alignment_and_validation():
+    rows = _rows([1000, 333], [S.BF16, S.F16])
+    lp = BASE * 5
+    # working copies aligned with p: vector path kept; misaligned by one element:
+    # the head absorbs it only if all buffers agree, else scalar fallback
+    r0 = rows[0] + (lp, S.BF16)
+    r1 = rows[1] + (lp + 4096, S.F16)
+    segs, info = S.debug_plan([r0, r1], 1, 2)
+    assert info.scalar_segments == 0
+    r1b = rows[1] + (lp + 4096 + 2, S.F16)
+    segs, info = S.debug_plan([r0, r1b], 1, 2)
+    assert info.scalar_segments == 1 and sum(s.numel for s in segs if s.tensor == 1) == 333
+    with pytest.raises(S.SomaoptError, match="lowp_dtype"):
+        S.debug_plan([rows[0] + (lp, S.F32)], 1, 2)
+    with pytest.raises(S.SomaoptError, match="reserved"):
+        S.debug_plan([rows[0] + (lp, S.BF16, 7)], 1, 2)
+    with pytest.raises(S.SomaoptError, match="aligned"):
+        S.debug_plan([rows[0] + (lp + 1, S.BF16)], 1, 2)
+    # a working copy may not overlap any other written buffer or a gradient
+    with pytest.raises(S.SomaoptError, match="overlap"):
+        S.debug_plan([rows[0] + (rows[0][2], S.BF16)], 1, 2)
+    with pytest.raises(S.SomaoptError, match="overlap"):
+        S.debug_plan([rows[0] + (rows[0][1], S.BF16)], 1, 2)
+
+
+def test_fp16_gradients_plan_like_bf16():
+    rows = _rows([4096, 4097], [S.F16, S.BF16])
+    s1, _ = S.debug_plan(rows, 1, 1)
+    assert all(s.vec_elems == 8 for s in s1)
+    assert [s.nvec for s in s1] == [512, 512] and s1[1].tail == 1
+
+
 def test_validation_overlaps():
     rows = _rows([64, 64])
     # p of tensor 1 aliases m of tensor 0

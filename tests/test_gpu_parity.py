@@ -343,3 +343,50 @@ class _Fake:
 
     def numel(self):
         return self.n
+
+
+@pytest.mark.parametrize("gdt,ldt", [(W.BF16, W.BF16), (W.F16, W.F16), (W.F32, W.BF16), (W.F16, W.BF16)])
+def test_working_copy_and_gradient_dtypes(gdt, ldt):
+    """bf16/fp16 working copies of the fp32 master (RLinf FP32MasterAdamW
+    reading) and fp16 gradients.  The copy must equal the round-to-nearest-even
+    of the kernel's own fp32 master bit for bit, and lie within one unit of the
+    copy rounded from the oracle's weights."""
+    import dataclasses
+    import oracle as O
+    from parity_util import DeviceState
+    base = W.action_expert(blocks=1, d=256, mlp=512, steps=4)
+    base.tensors = [dataclasses.replace(t, grad_dtype=gdt) for t in base.tensors]
+    wl = base
+    log(f"[parity] working copy grad={gdt} copy={ldt}")
+    st = allocate(wl)
+    ldtype = W.torch_dtype(ldt)
+    lowp = [torch.full((t.numel,), float("nan"), dtype=ldtype, device="cuda") for t in wl.tensors]
+    p0 = [host(x) for x in st.p]
+    from tensor_optimizer_step_amd.somaopt import FusedAdamW
+    opt = FusedAdamW(st.p, st.g, st.m, st.v, [t.group for t in wl.tensors], wl.groups, wl.max_norm,
+                     wl.grad_divisor, params_lowp=lowp)
+    ora = make_oracle(wl, p0)
+    opt.capture()
+    for k in range(1, wl.steps + 1):
+        fill_grads(wl, st, k)
+        grads = [host(g) for g in st.g]
+        opt.replay()
+        s, _ = opt.read_stats()
+        want = ora.step(grads)
+        assert_norm(s.norm, want.norm)
+    torch.cuda.synchronize()
+    for i in range(wl.n_tensors):
+        gp = host(st.p[i])
+        assert_close(f"p[{i}]", gp, ora.p[i])
+        assert_close(f"m[{i}]", host(st.m[i]), ora.m[i])
+        assert_close(f"v[{i}]", host(st.v[i]), ora.v[i])
+        got = lowp[i].cpu().view(torch.int16).numpy().view(np.uint16)
+        if ldt == W.BF16:
+            mine = O.round_to_bf16_bits(gp)
+            theirs = O.round_to_bf16_bits(ora.p[i].astype(np.float32))
+        else:
+            mine = O.round_to_f16(gp).view(np.uint16)
+            theirs = O.round_to_f16(ora.p[i].astype(np.float32)).view(np.uint16)
+        assert np.array_equal(got, mine), f"working copy {i} differs from RNE of the fp32 master"
+        assert np.abs(got.astype(np.int32) - theirs.astype(np.int32)).max() <= 1
+    opt.close()

@@ -217,6 +217,40 @@ def pin_bf16_widening():
     assert np.isnan(nan[0])
 
 
+def pin_fp16_widening():
+    vals = np.array([1.0, -2.5, 65504.0, 2.0 ** -24, -0.0, np.inf], np.float16)
+    got = OA.widen_grad(vals)
+    assert got.dtype == np.float64 and got.tolist() == [1.0, -2.5, 65504.0, 2.0 ** -24, -0.0, math.inf]
+
+
+def pin_bf16_working_copy_rounding():
+    """RNE fp32 -> bf16: exact ties, carries into the exponent, NaN; and the
+    library special case torch .to(torch.bfloat16) on random values."""
+    def f32(bits):
+        return np.array([bits], np.uint32).view(np.float32)
+    cases = {
+        0x3F808000: 0x3F80,   # tie, even lower half kept
+        0x3F818000: 0x3F82,   # tie, odd -> rounds up to even
+        0x3F808001: 0x3F81,   # just above the tie
+        0x3F807FFF: 0x3F80,   # just below the tie
+        0x3FFF8000: 0x4000,   # tie that carries into the exponent
+        0x7F7FFFFF: 0x7F80,   # largest finite rounds to infinity
+        0x80000001: 0x8000,   # tiny negative subnormal -> -0
+        0x7F800000: 0x7F80,   # +inf stays
+    }
+    for bits, want in cases.items():
+        assert int(OA.round_to_bf16_bits(f32(bits))[0]) == want, hex(bits)
+    assert int(OA.round_to_bf16_bits(np.array([np.nan], np.float32))[0]) == 0x7FC0
+    torch = pytest.importorskip("torch")
+    x = (_rng(22).standard_normal(100000) * 10.0 ** _rng(23).integers(-30, 30, 100000)).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(OA.round_to_bf16_bits(x), ref)
+    # fp16 working copy: numpy's conversion agrees with torch's
+    y = (x / 1e20).astype(np.float32)
+    assert np.array_equal(OA.round_to_f16(y).view(np.uint16),
+                          torch.from_numpy(y).to(torch.float16).numpy().view(np.uint16))
+
+
 def pin_inputs_untouched_and_frozen_skipped():
     rng = _rng(19)
     ps = [rng.normal(0, 0.02, size=n).astype(np.float32) for n in (5, 7, 9)]
@@ -305,7 +339,8 @@ PINS = [pin_norm_exact_example, pin_norm_decimal_bruteforce, pin_norm_reorder_in
         pin_norm_owner_shards, pin_clip_coefficient, pin_step1_closed_form,
         pin_two_step_moments, pin_constant_gradient_closed_form, pin_pure_decay,
         pin_lr_zero_is_identity, pin_bf16_widening, pin_inputs_untouched_and_frozen_skipped,
-        pin_nonfinite, pin_resume_equals_continuation, pin_torch_cpu_float64]
+        pin_nonfinite, pin_resume_equals_continuation, pin_torch_cpu_float64, pin_fp16_widening,
+        pin_bf16_working_copy_rounding]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -384,6 +419,15 @@ def _widen_shift15(g):
     return g.astype(np.float64)
 
 
+def _round_truncate(x):
+    return (np.asarray(x, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _round_half_up(x):
+    u = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x8000) >> 16).astype(np.uint16)
+
+
 _REAL = {"normalized_sumsq": OA.normalized_sumsq, "adamw_update": OA.adamw_update}
 
 MUTANTS = {
@@ -400,6 +444,8 @@ MUTANTS = {
     "clip_without_eps": ("clip_coefficient", _clip_no_eps),
     "clip_not_clamped": ("clip_coefficient", _clip_no_clamp),
     "bf16_widen_wrong_shift": ("widen_grad", _widen_shift15),
+    "bf16_round_truncates": ("round_to_bf16_bits", _round_truncate),
+    "bf16_round_half_up": ("round_to_bf16_bits", _round_half_up),
 }
 
 
