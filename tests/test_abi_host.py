@@ -241,3 +241,13 @@ def test_validation_n_groups():
         S.debug_plan(_rows([4]), 0, 2)
     with pytest.raises(S.SomaoptError):
         S.debug_plan(_rows([4]), S.MAX_GROUPS + 1, 2)
+
+
+def test_bench_refuses_several_gpus():
+    import subprocess
+    import sys
+    bench = os.path.join(ROOT, "bench.py")
+    r = subprocess.run([sys.executable, bench, "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr

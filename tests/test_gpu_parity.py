@@ -390,3 +390,50 @@ def test_working_copy_and_gradient_dtypes(gdt, ldt):
         assert np.array_equal(got, mine), f"working copy {i} differs from RNE of the fp32 master"
         assert np.abs(got.astype(np.int32) - theirs.astype(np.int32)).max() <= 1
     opt.close()
+
+
+def test_setters_mid_run_and_side_stream():
+    """Change max_norm / divisor and the hyperparameters between steps, reset
+    the step count on a live handle, and run everything on a non-default
+    stream; the oracle follows the same settings."""
+    import oracle as O
+    wl = W.tiny(seed_offset=7, n_tensors=20, max_numel=30000)
+    st = allocate(wl)
+    p0 = [host(x) for x in st.p]
+    side = torch.cuda.Stream()
+    opt = make_handle(wl, st, stream=side)
+    ora = make_oracle(wl, p0)
+    opt.capture()
+    plan = [  # (max_norm, divisor, lr, wd, beta1, beta2, eps, set_step)
+        (1.0, 4.0, 5e-6, 0.01, 0.9, 0.999, 1e-8, None),
+        (0.05, 4.0, 1e-4, 0.1, 0.9, 0.999, 1e-8, None),
+        (10.0, 2.0, 1e-3, 0.0, 0.8, 0.99, 1e-6, None),
+        (1.0, 16.0, 1e-3, 0.05, 0.95, 0.9999, 1e-8, 7),
+        (0.5, 1.0, 2e-4, 0.01, 0.9, 0.999, 1e-8, 123456),
+        (0.5, 1.0, 2e-4, 0.01, 0.9, 0.999, 1e-8, None),
+    ]
+    for k, (M, D, lr, wd, b1, b2, eps, reset) in enumerate(plan, start=1):
+        fill_grads(wl, st, k)
+        torch.cuda.synchronize()
+        grads = [host(g) for g in st.g]
+        with torch.cuda.stream(side):
+            opt.set_clip(M, D, side)
+            opt.set_groups([W.GroupHP(lr, wd, b1, b2, eps)], side)
+            if reset is not None:
+                opt.set_step(reset, side)
+            opt.replay(side)
+        s, t = opt.read_stats(side)
+        ora.max_norm, ora.grad_divisor = M, D
+        ora.groups[0] = O.Group(lr, wd, b1, b2, eps)
+        if reset is not None:
+            ora.t = [reset]
+        want = ora.step(grads)
+        assert_norm(s.norm, want.norm)
+        assert s.clip_coef == pytest.approx(want.coef, rel=1e-12)
+        assert t == ora.t
+    torch.cuda.synchronize()
+    for i in range(wl.n_tensors):
+        assert_close(f"p[{i}]", host(st.p[i]), ora.p[i])
+        assert_close(f"m[{i}]", host(st.m[i]), ora.m[i])
+        assert_close(f"v[{i}]", host(st.v[i]), ora.v[i])
+    opt.close()
