@@ -269,6 +269,10 @@ int somaopt_init_tensor_table(const somaopt_tensor_desc* descs, int64_t n_tensor
     Plan p2 = build_plan(descs, n_tensors, 2, ch2);
     if (p1.segs.size() >= 0xFFFFFFFFull || p2.segs.size() >= 0xFFFFFFFFull)
         return fail(SOMAOPT_E_INVALID, "too many segments for 32-bit indices");
+    // A dispatch holds fewer than 2^32 work-items.
+    if ((uint64_t)p1.n_blocks() * kPass1Threads >= 0xFFFFFFFFull ||
+        (uint64_t)p2.n_blocks() * kPass2Threads >= 0xFFFFFFFFull)
+        return fail(SOMAOPT_E_INVALID, "table too large for one dispatch (raise SOMAOPT_PASS*_CHUNK)");
     // The norm pass always runs at least one workgroup so that the statistics
     // are produced even when nothing is owned.
     if (p1.block_first.size() < 2) p1.block_first = {0u, 0u};
