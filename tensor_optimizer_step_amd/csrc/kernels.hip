@@ -4,7 +4,8 @@
 // its block with 16-byte loads, squares and accumulates in fp64, reduces across
 // the wavefront with DPP row permutes and across waves through LDS, and stores
 // one partial per workgroup.  A one-workgroup finalize kernel then adds the
-// partials in a fixed order, so the global sum is bitwise reproducible, and
+// partials in a fixed order (through one intermediate level of fixed-order
+// workgroup sums for large tables), so the global sum is bitwise reproducible, and
 // derives the norm, the clip coefficient and each group's bias-corrected
 // constants on the device (no host synchronization).  SomaSpeed landing page,
 // paragraph "SomaSpeed batches that work across tensors ...": statistics for
@@ -262,30 +263,50 @@ __global__ __launch_bounds__(BS) void sqnorm_pass1(Pass1Args a) {
     if (tid == 0) a.partials[b] = part;
 }
 
-// One workgroup: fixed-order sum of the partials (per-thread strided sums, then
-// the fixed wave/LDS tree), then the statistics and
-// the per-group constants of the pending update.  The kernel boundary after
-// the norm pass makes every partial visible without any cache maintenance.
+// Fixed-order sum of n doubles by one workgroup (valid in thread 0): thread t
+// adds elements t, t + BS, t + 2 BS, ... in increasing order, sixteen loads in
+// flight at a time, then the fixed wave/LDS tree.
 template <int BS>
-__global__ __launch_bounds__(BS) void sqnorm_finalize(Pass1Args a) {
-    __shared__ double lds[BS / 64];
-    const int tid = threadIdx.x;
-    const AS_GLOBAL double* part = gptr<double>(a.partials);
-    // Thread t adds partials t, t + BS, t + 2 BS, ... in increasing order; the
-    // loads of sixteen consecutive strides are issued together to overlap their
-    // latency, the additions stay in that fixed order.
+__device__ __forceinline__ double fixed_order_sum(const AS_GLOBAL double* part, uint32_t n, double* lds) {
     constexpr int kLoads = 16;
+    const uint32_t tid = threadIdx.x;
     double acc = 0.0;
     uint32_t i = tid;
-    for (; i + (kLoads - 1) * BS < a.n_blocks; i += kLoads * BS) {
+    for (; i + (kLoads - 1) * BS < n; i += kLoads * BS) {
         double x[kLoads];
 #pragma unroll
         for (int k = 0; k < kLoads; ++k) x[k] = part[i + k * BS];
 #pragma unroll
         for (int k = 0; k < kLoads; ++k) acc += x[k];
     }
-    for (; i < a.n_blocks; i += BS) acc += part[i];
-    const double total = block_sum<BS>(acc, lds);
+    for (; i < n; i += BS) acc += part[i];
+    return block_sum<BS>(acc, lds);
+}
+
+// First level for large tables: workgroup j sums partials
+// [j * kReduceSpan, (j + 1) * kReduceSpan) in fixed order.
+template <int BS>
+__global__ __launch_bounds__(BS) void reduce_partials(Pass1Args a) {
+    __shared__ double lds[BS / 64];
+    const uint32_t j = blockIdx.x;
+    const uint32_t first = j * kReduceSpan;
+    const uint32_t n = min(kReduceSpan, a.n_blocks - first);
+    const double s = fixed_order_sum<BS>(gptr<double>(a.partials) + first, n, lds);
+    if (threadIdx.x == 0) a.partials2[j] = s;
+}
+
+// One workgroup: fixed-order sum of the (first- or second-level) partials,
+// then the statistics and the per-group constants of the pending update.  The
+// kernel boundary after the norm pass makes every partial visible without any
+// cache maintenance.
+template <int BS>
+__global__ __launch_bounds__(BS) void sqnorm_finalize(Pass1Args a) {
+    __shared__ double lds[BS / 64];
+    const int tid = threadIdx.x;
+    const bool two = a.n_blocks > kTwoLevelAbove;
+    const double* src = two ? a.partials2 : a.partials;
+    const uint32_t n = two ? (a.n_blocks + kReduceSpan - 1) / kReduceSpan : a.n_blocks;
+    const double total = fixed_order_sum<BS>(gptr<double>(src), n, lds);
     if (tid == 0) finalize_stats(a.state, total);
     if (tid < a.n_groups) finalize_group(a.state, tid, a.advance);
 }
@@ -483,6 +504,12 @@ hipError_t launch_pass1(const Pass1Args& a, hipStream_t s) {
     hipLaunchKernelGGL(sqnorm_pass1<kPass1Threads>, dim3(a.n_blocks), dim3(kPass1Threads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (a.n_blocks > kTwoLevelAbove) {
+        const uint32_t groups = (a.n_blocks + kReduceSpan - 1) / kReduceSpan;
+        hipLaunchKernelGGL(reduce_partials<kReduceThreads>, dim3(groups), dim3(kReduceThreads), 0, s, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(sqnorm_finalize<kFinalizeThreads>, dim3(1), dim3(kFinalizeThreads), 0, s, a);
     return hipGetLastError();
 }

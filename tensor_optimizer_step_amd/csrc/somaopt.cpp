@@ -31,6 +31,7 @@ struct somaopt_handle {
     uint32_t* d_blk2 = nullptr;
     uint32_t nblk2 = 0;
     double* d_partials = nullptr;
+    double* d_partials2 = nullptr;
     DevState* d_state = nullptr;
     bool pending = false;          // a norm pass opened an update not yet applied
     hipStream_t cap_stream = nullptr;
@@ -147,7 +148,7 @@ void free_handle(somaopt_handle* h) {
     if (!h) return;
     if (h->exec) (void)hipGraphExecDestroy(h->exec);
     if (h->cap_stream) (void)hipStreamDestroy(h->cap_stream);
-    void* bufs[] = {h->d_seg1, h->d_blk1, h->d_seg2, h->d_blk2, h->d_partials, h->d_state};
+    void* bufs[] = {h->d_seg1, h->d_blk1, h->d_seg2, h->d_blk2, h->d_partials, h->d_partials2, h->d_state};
     for (void* p : bufs)
         if (p) (void)hipFree(p);
     delete h;
@@ -187,6 +188,7 @@ int launch_norm_pass(somaopt_handle* h, int advance, hipStream_t s) {
     a.blk_first = h->d_blk1;
     a.n_blocks = h->nblk1;
     a.partials = h->d_partials;
+    a.partials2 = h->d_partials2;
     a.state = h->d_state;
     a.n_groups = h->n_groups;
     a.advance = advance;
@@ -338,6 +340,8 @@ int somaopt_init_tensor_table(const somaopt_tensor_desc* descs, int64_t n_tensor
     if ((e = alloc_upload(&h->d_state, stv, s)) != hipSuccess ||
         (e = hipMalloc(reinterpret_cast<void**>(&h->d_partials), sizeof(double) * std::max<uint32_t>(h->nblk1, 1))) !=
             hipSuccess ||
+        (e = hipMalloc(reinterpret_cast<void**>(&h->d_partials2),
+                       sizeof(double) * ((h->nblk1 + kReduceSpan - 1) / kReduceSpan + 1))) != hipSuccess ||
         (e = hipStreamSynchronize(s)) != hipSuccess) {
         free_handle(h);
         return e == hipErrorOutOfMemory ? fail(SOMAOPT_E_NOMEM, "device allocation failed")

@@ -437,3 +437,14 @@ def test_setters_mid_run_and_side_stream():
         assert_close(f"m[{i}]", host(st.m[i]), ora.m[i])
         assert_close(f"v[{i}]", host(st.v[i]), ora.v[i])
     opt.close()
+
+
+@pytest.mark.parametrize("chunks", [(256, 256), (512, 4096), (65536, 1024)])
+def test_other_chunkings_and_two_level_reduction(chunks, monkeypatch):
+    """Other workgroup sizes (env tuning knobs), including the two-level
+    reduction of norm partials (more than 8192 workgroups)."""
+    monkeypatch.setenv("SOMAOPT_PASS1_CHUNK", str(chunks[0]))
+    monkeypatch.setenv("SOMAOPT_PASS2_CHUNK", str(chunks[1]))
+    wl = W.launch_bound(n_tensors=3000)
+    wl.steps = 3
+    st, ora = run_and_compare(wl)
