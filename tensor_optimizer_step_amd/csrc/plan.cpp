@@ -149,7 +149,7 @@ int64_t common_head(const uintptr_t* addr, const int64_t* esz, int n, int64_t ve
 
 }  // namespace
 
-Plan build_plan(const somaopt_tensor_desc* d, int64_t n, int pass, int64_t chunk) {
+Plan build_plan(const somaopt_tensor_desc* d, int64_t n, int pass, int64_t chunk, int64_t segment_cost) {
     Plan plan;
     plan.chunk = chunk;
     for (int64_t i = 0; i < n; ++i) {
@@ -198,8 +198,8 @@ Plan build_plan(const somaopt_tensor_desc* d, int64_t n, int pass, int64_t chunk
     plan.block_first.clear();
     int64_t cost = 0;
     for (size_t s = 0; s < plan.segs.size(); ++s) {
-        int64_t c = plan.segs[s].numel + kSegmentCost;
-        if (plan.block_first.empty() || cost + c > chunk + kSegmentCost) {
+        int64_t c = plan.segs[s].numel + segment_cost;
+        if (plan.block_first.empty() || cost + c > chunk + segment_cost) {
             plan.block_first.push_back((uint32_t)s);
             cost = 0;
         }

@@ -116,10 +116,11 @@ def test_plan_covers_every_element_once(pass_):
     assert info.owned_numel == sum(s for s, t, o in zip(sizes, tr, ow) if t and o)
     assert info.n_trainable == sum(tr)
     # workgroup cost bound
+    cost = 1024   # per-segment packing cost of the planner
     per_block = {}
     for s in segs:
-        per_block[s.block] = per_block.get(s.block, 0) + s.numel + 64
-    assert max(per_block.values()) <= chunk + 64
+        per_block[s.block] = per_block.get(s.block, 0) + s.numel + cost
+    assert max(per_block.values()) <= chunk + cost
 
 
 def test_plan_aligned_tensors_use_vectors():
