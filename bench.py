@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="action_expert",
-                    choices=["action_expert", "backbone_7b", "launch_bound", "tiny"])
+                    choices=["action_expert", "backbone_7b", "sharded_7b", "launch_bound", "tiny"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     ap.add_argument("--lowp", choices=["none", "bf16", "f16"], default="none",
@@ -131,6 +131,63 @@ def load_traffic(workload: str, algo_bytes: int):
     return rec.get("hbm_bytes_per_launch")
 
 
+def plain_setup(torch, somaopt, W, wl, dev, stream, lowp_dtype):
+    """One allocation per tensor: seeded fp32 weights, zero moments, step-1 grads."""
+    print(f"[bench] {wl.name}: {wl.n_tensors} tensors, {wl.trainable_numel} trainable elements",
+          file=sys.stderr, flush=True)
+    p, g, m, v = [], [], [], []
+    for i, t in enumerate(wl.tensors):
+        p.append(W.param_values(wl, i, dev))
+        g.append(W.grad_values(wl, i, 1, dev))
+        m.append(torch.zeros(t.numel, device=dev))
+        v.append(torch.zeros(t.numel, device=dev))
+    lowp = None
+    if lowp_dtype != "none":
+        lowp = [torch.empty(t.numel, dtype=W.torch_dtype(lowp_dtype), device=dev) for t in wl.tensors]
+    opt = somaopt.FusedAdamW(p, g, m, v, [t.group for t in wl.tensors], wl.groups, wl.max_norm,
+                             wl.grad_divisor, trainable=[t.trainable for t in wl.tensors],
+                             stream=stream, params_lowp=lowp)
+    return (p, g, m, v, lowp), opt
+
+
+def sharded_setup(torch, somaopt, W, dev, stream, lowp_dtype):
+    """The 7B state cut into four contiguous shard allocations on one device,
+    RMSNorms replicated in every shard and owned by shard 0 (one descriptor per
+    piece or replica).  Returns a workload view whose tensors are the pieces."""
+    lay = W.sharded_7b()
+    base = lay.base
+    print(f"[bench] sharded_7b: {lay.n_descriptors} descriptors over {lay.n_shards} shards, "
+          f"{sum(q.numel for q in lay.pieces)} updated elements", file=sys.stderr, flush=True)
+    bufs = {k: [] for k in "pgmv"}
+    for n in lay.shard_numel:
+        bufs["p"].append(torch.empty(n, device=dev))
+        bufs["g"].append(torch.empty(n, dtype=torch.bfloat16, device=dev))
+        bufs["m"].append(torch.zeros(n, device=dev))
+        bufs["v"].append(torch.zeros(n, device=dev))
+    by_tensor = {}
+    for q in lay.pieces:
+        by_tensor.setdefault(q.tensor, []).append(q)
+    for i in range(base.n_tensors):
+        pv, gv = W.param_values(base, i, dev), W.grad_values(base, i, 1, dev)
+        for q in by_tensor[i]:
+            sl = slice(q.s_offset, q.s_offset + q.numel)
+            bufs["p"][q.shard][sl].copy_(pv[q.t_offset:q.t_offset + q.numel])
+            bufs["g"][q.shard][sl].copy_(gv[q.t_offset:q.t_offset + q.numel])
+    views = {k: [bufs[k][q.shard][q.s_offset:q.s_offset + q.numel] for q in lay.pieces] for k in "pgmv"}
+    lowp = None
+    if lowp_dtype != "none":
+        lowp = [torch.empty(q.numel, dtype=W.torch_dtype(lowp_dtype), device=dev) for q in lay.pieces]
+    opt = somaopt.FusedAdamW(views["p"], views["g"], views["m"], views["v"],
+                             [base.tensors[q.tensor].group for q in lay.pieces], base.groups,
+                             base.max_norm, base.grad_divisor, owner=[q.owner for q in lay.pieces],
+                             stream=stream, params_lowp=lowp)
+    pieces = [W.TensorSpec(f"piece{j}", q.numel, base.tensors[q.tensor].group, W.BF16)
+              for j, q in enumerate(lay.pieces)]
+    import dataclasses
+    wl = dataclasses.replace(base, name="sharded_7b", tensors=pieces)
+    return wl, opt, (bufs, views, lowp)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -149,26 +206,21 @@ def main():
     from tensor_optimizer_step_amd import workloads as W
 
     somaopt.load()
-    wl = W.WORKLOADS[args.workload]()
     dev = "cuda"
-    print(f"[bench] {wl.name}: {wl.n_tensors} tensors, {wl.trainable_numel} trainable elements",
-          file=sys.stderr, flush=True)
-    p, g, m, v = [], [], [], []
-    for i, t in enumerate(wl.tensors):
-        p.append(W.param_values(wl, i, dev))
-        g.append(W.grad_values(wl, i, 1, dev))
-        m.append(torch.zeros(t.numel, device=dev))
-        v.append(torch.zeros(t.numel, device=dev))
     stream = torch.cuda.current_stream()
-    lowp = None
-    if args.lowp != "none":
-        lowp = [torch.empty(t.numel, dtype=W.torch_dtype(args.lowp), device=dev) for t in wl.tensors]
-    opt = somaopt.FusedAdamW(p, g, m, v, [t.group for t in wl.tensors], wl.groups, wl.max_norm,
-                             wl.grad_divisor, trainable=[t.trainable for t in wl.tensors],
-                             stream=stream, params_lowp=lowp)
+    if args.workload == "sharded_7b":
+        wl, opt, keep = sharded_setup(torch, somaopt, W, dev, stream, args.lowp)
+    else:
+        wl = W.WORKLOADS[args.workload]()
+        keep, opt = plain_setup(torch, somaopt, W, wl, dev, stream, args.lowp)
     info = opt.plan_info()
     opt.capture()
-    bts = bytes_per_step(wl, lowp is not None)
+    bts = bytes_per_step(wl, args.lowp != "none")
+    if args.workload == "sharded_7b":
+        # the norm pass reads only owned gradients (replicas are skipped)
+        info_owned = info.owned_numel
+        bts["pass1"] = 2 * info_owned
+        bts["total"] = bts["pass1"] + bts["pass2"]
     n_elem = wl.trainable_numel
 
     # warm-up, then exactly K timed replays of the captured step
@@ -206,7 +258,7 @@ def main():
         raise RuntimeError("non-finite statistics in the benchmark run")
 
     p2_gbs = bts["pass2"] / (p2_ms * 1e-3) / 1e9
-    traffic = load_traffic(wl.name, bts["pass2"]) if lowp is None else None
+    traffic = load_traffic(wl.name, bts["pass2"]) if args.lowp == "none" else None
     roofline = {"bound": "hbm", "achieved": round(p2_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(p2_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "adamw_pass2", "algorithmic_bytes_per_launch": bts["pass2"],
@@ -214,7 +266,7 @@ def main():
                 "pass1_avg_launch_ms": round(p1_ms, 5),
                 "pass1_GBps": round(bts["pass1"] / (p1_ms * 1e-3) / 1e9, 1)}
     cpu = None
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and args.workload != "sharded_7b":
         cpu = cpu_baseline(wl, args.cpu_seconds)
     model_gbs = bts["total"] / step_s / 1e9
     out = {
@@ -241,6 +293,7 @@ def main():
         "cpu_baseline": cpu,
     }
     opt.close()
+    del keep
     print(json.dumps(out), flush=True)
 
 
