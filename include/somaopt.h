@@ -239,6 +239,48 @@ int64_t somaopt_debug_plan(const somaopt_tensor_desc* descs, int64_t n_tensors, 
                            int32_t pass, int64_t pass1_chunk, int64_t pass2_chunk,
                            somaopt_plan_segment* segs, int64_t cap, somaopt_plan_info* info);
 
+/* ------------------------------------------------------------------------
+ * Tiled attention over frozen and trainable keys (SomaSpeed landing page,
+ * paragraph "Attention is the connection between the action computation and
+ * its context": keys and values are read tile by tile without storing the
+ * score matrix, and gradient work for frozen inputs is skipped).
+ *
+ * Per (batch b, head h): S = scale * Q K^T, P = softmax over keys, O = P V,
+ * LSE = log sum_j exp(S_ij).  Keys [0, lk_frozen) are frozen: the backward
+ * returns dQ for every query and dK, dV only for keys [lk_frozen, lk).
+ * Layout (all row-major, rows contiguous, base pointers 16-byte aligned):
+ *   q, o, d_o   bf16 [batch][heads][lq][head_dim]
+ *   k, v        bf16 [batch][heads][lk][head_dim]
+ *   lse, delta  fp32 [batch][heads][lq]
+ *   dq          fp32 [batch][heads][lq][head_dim]
+ *   dk, dv      fp32 [batch][heads][lk - lk_frozen][head_dim] (NULL allowed
+ *               when lk_frozen == lk)
+ * head_dim is 64 or 128; batch, heads <= 65535; lq, lk >= 1.  Products use
+ * bf16 matrix-core inputs (P and dS rounded once to bf16) with fp32
+ * accumulation.  Device pointers are caller-owned; the calls only enqueue
+ * work on `stream`.  SOMAOPT_E_INVALID on a bad shape, a NULL or misaligned
+ * pointer, or a buffer that is not device memory large enough for its shape.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+    int32_t batch;
+    int32_t heads;
+    int32_t lq;          /* queries per (batch, head)                           */
+    int32_t lk;          /* keys per (batch, head)                              */
+    int32_t lk_frozen;   /* leading frozen keys, 0 <= lk_frozen <= lk           */
+    int32_t head_dim;    /* 64 or 128                                           */
+    float scale;         /* score scale, usually 1 / sqrt(head_dim)             */
+} somaopt_attn_shape;
+
+/* Forward: writes O (bf16) and LSE (fp32, natural log). */
+int somaopt_attn_forward(const void* q, const void* k, const void* v, void* o, float* lse,
+                         const somaopt_attn_shape* shape, void* stream);
+
+/* Backward from the saved O and LSE: writes dQ, and dK, dV of the trainable
+ * keys; `delta` is a caller-provided fp32 [batch][heads][lq] workspace. */
+int somaopt_attn_backward(const void* q, const void* k, const void* v, const void* o,
+                          const float* lse, const void* d_o, float* dq, float* dk, float* dv,
+                          float* delta, const somaopt_attn_shape* shape, void* stream);
+
 /* Release the handle's device tables, graph and private stream.  Waits for
  * work the handle enqueued.  NULL is ignored. */
 void somaopt_destroy(somaopt_handle* h);

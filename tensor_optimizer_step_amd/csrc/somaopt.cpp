@@ -18,6 +18,10 @@
 #include "somaopt.h"
 #include "state.hpp"
 
+namespace somaopt {
+int set_error(int code, const std::string& msg);
+}  // namespace somaopt
+
 using namespace somaopt;
 
 struct somaopt_handle {
@@ -208,6 +212,8 @@ int launch_update_pass(somaopt_handle* h, hipStream_t s) {
 }
 
 }  // namespace
+
+int somaopt::set_error(int code, const std::string& msg) { return fail(code, msg); }
 
 extern "C" {
 

@@ -62,6 +62,12 @@ class PlanSegment(ctypes.Structure):
                 ("vec_elems", ctypes.c_int32), ("block", ctypes.c_int32)]
 
 
+class AttnShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("lq", ctypes.c_int32),
+                ("lk", ctypes.c_int32), ("lk_frozen", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("scale", ctypes.c_float)]
+
+
 _P = ctypes.c_void_p
 _PP = ctypes.POINTER(ctypes.c_void_p)
 # name -> (restype, argtypes); mirrors include/somaopt.h
@@ -85,6 +91,9 @@ SIGNATURES = {
                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                             ctypes.c_int64, ctypes.POINTER(PlanSegment),
                                             ctypes.c_int64, ctypes.POINTER(PlanInfo)]),
+    "somaopt_attn_forward": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.POINTER(AttnShape), _P]),
+    "somaopt_attn_backward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                             ctypes.POINTER(AttnShape), _P]),
     "somaopt_destroy": (None, [_P]),
     "somaopt_last_error": (ctypes.c_char_p, []),
     "somaopt_version": (ctypes.c_char_p, []),
@@ -298,6 +307,33 @@ class FusedAdamW:
             self.close()
         except Exception:
             pass
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def attn_shape(q, k, lk_frozen: int, scale: Optional[float] = None) -> AttnShape:
+    """Shape of bf16 q [B, H, Lq, D] and k [B, H, Lk, D]."""
+    b, h, lq, d = q.shape
+    lk = k.shape[2]
+    return AttnShape(b, h, lq, lk, int(lk_frozen), d, float(scale if scale is not None else d ** -0.5))
+
+
+def attn_forward(q, k, v, o, lse, lk_frozen: int = 0, scale: Optional[float] = None, stream=None):
+    """O (bf16, same shape as q) and LSE (fp32 [B, H, Lq]) of softmax attention."""
+    sh = attn_shape(q, k, lk_frozen, scale)
+    _check(load().somaopt_attn_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                       ctypes.byref(sh), _stream_ptr(stream)))
+
+
+def attn_backward(q, k, v, o, lse, d_o, dq, dk, dv, delta, lk_frozen: int,
+                  scale: Optional[float] = None, stream=None):
+    """dQ for every query; dK, dV (fp32 [B, H, Lk - lk_frozen, D]) for the trainable keys."""
+    sh = attn_shape(q, k, lk_frozen, scale)
+    _check(load().somaopt_attn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(d_o),
+                                        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta), ctypes.byref(sh),
+                                        _stream_ptr(stream)))
 
 
 def version() -> str:
