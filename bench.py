@@ -38,7 +38,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="action_expert",
-                    choices=["action_expert", "backbone_7b", "sharded_7b", "launch_bound", "tiny"])
+                    choices=["action_expert", "backbone_7b", "sharded_7b", "launch_bound", "tiny",
+                             "frozen_attention"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     ap.add_argument("--lowp", choices=["none", "bf16", "f16"], default="none",
@@ -188,6 +189,83 @@ def sharded_setup(torch, somaopt, W, dev, stream, lowp_dtype):
     return wl, opt, (bufs, views, lowp)
 
 
+ATTN_SHAPE = dict(batch=64, heads=8, lq=64, lk=1024, lk_frozen=960, head_dim=128)
+
+
+def attention_bench(torch, args):
+    """Tiled attention with a frozen context prefix (one JSON line).
+
+    Action-token queries (64) attend to 960 frozen context keys plus 64
+    trainable action keys per (batch, head); 64 x 8 heads of dimension 128.
+    Times the forward and the backward (dQ for all queries, dK/dV only for the
+    trainable keys), and the backward with every key trainable for contrast.
+    """
+    import math
+    from tensor_optimizer_step_amd import somaopt
+    somaopt.load()
+    sh = ATTN_SHAPE
+    b, h, lq, lk, lf, d = (sh[k] for k in ("batch", "heads", "lq", "lk", "lk_frozen", "head_dim"))
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4000)
+    mk = lambda *x: torch.randn(*x, generator=gen, device="cuda").to(torch.bfloat16)
+    q, k, v, do = mk(b, h, lq, d), mk(b, h, lk, d), mk(b, h, lk, d), mk(b, h, lq, d)
+    o = torch.empty_like(q)
+    lse = torch.empty(b, h, lq, device="cuda")
+    dq = torch.empty(b, h, lq, d, device="cuda")
+    delta = torch.empty(b, h, lq, device="cuda")
+    dk_all = torch.empty(b, h, lk, d, device="cuda")
+    dv_all = torch.empty(b, h, lk, d, device="cuda")
+    dk, dv = dk_all[:, :, : lk - lf].contiguous(), dv_all[:, :, : lk - lf].contiguous()
+    scale = 1.0 / math.sqrt(d)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        for _ in range(max(args.warmup, 1)):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    fwd = lambda: somaopt.attn_forward(q, k, v, o, lse, lf, scale, stream)
+    bwd = lambda: somaopt.attn_backward(q, k, v, o, lse, do, dq, dk, dv, delta, lf, scale, stream)
+    bwd_all = lambda: somaopt.attn_backward(q, k, v, o, lse, do, dq, dk_all, dv_all, delta, 0, scale, stream)
+    t0 = time.perf_counter()
+    ms_f = timed(fwd, args.steps)
+    ms_b = timed(bwd, args.steps)
+    ms_ball = timed(bwd_all, args.steps)
+    wall = time.perf_counter() - t0
+    bh, lt = b * h, lk - lf
+    bytes_f = bh * (2 * lq * d * 2 + 2 * lk * d * 2) + bh * lq * 4
+    # minimum traffic: every input read once, every output written once
+    bytes_b = bh * (3 * lq * d * 2 + 2 * lq * 4 + 2 * lk * d * 2   # q, dO, o, lse; k, v
+                    + lq * d * 4 + lq * 4                           # dq, delta
+                    + 2 * lt * d * 4)                               # dk, dv (trainable keys)
+    flops_f = 4.0 * bh * lq * lk * d
+    flops_b = bh * (6.0 * lq * lk * d + 4.0 * lq * lt * d)       # S, dP, dQ over all keys; dK, dV over trainable
+    flops_ball = bh * (6.0 * lq * lk * d + 4.0 * lq * lk * d)
+    out = {
+        "metric": "tiled attention with a frozen context: forward + backward time (us) and achieved HBM GB/s",
+        "value": (ms_f + ms_b) * 1e3, "unit": "us per forward+backward", "higher_is_better": False,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "data": "synthetic", "dtype": "bf16",
+        "config": {"workload": "frozen_attention", **sh},
+        "forward": {"ms": ms_f, "GBps": bytes_f / ms_f / 1e6, "TFLOPs": flops_f / ms_f / 1e9,
+                    "algorithmic_bytes": bytes_f},
+        "backward": {"ms": ms_b, "GBps": bytes_b / ms_b / 1e6, "TFLOPs": flops_b / ms_b / 1e9,
+                     "algorithmic_bytes": bytes_b},
+        "backward_all_keys_trainable": {"ms": ms_ball, "TFLOPs": flops_ball / ms_ball / 1e9},
+        "roofline": {"bound": "hbm", "achieved": round(bytes_f / ms_f / 1e6, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(bytes_f / ms_f / 1e6 / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "attn_fwd"},
+        "wall_s": wall,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -200,6 +278,9 @@ def main():
         sys.exit(1)
     if args.copy_calibration:
         copy_calibration(torch)
+        return
+    if args.workload == "frozen_attention":
+        attention_bench(torch, args)
         return
 
     from tensor_optimizer_step_amd import somaopt

@@ -72,47 +72,84 @@ __device__ __forceinline__ float group_max(float x) {
 
 __device__ __forceinline__ u32x4 load16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 
-// Rows [row0, row0 + 64) of a [L][D] bf16 matrix into a row-major LDS tile;
-// rows at or past L are zero.
+// Rows [row0, row0 + 64) of a [L][D] bf16 matrix, as held by one thread
+// between its global loads and its LDS stores (so the loads of the next tile
+// can be in flight while the current tile is computed).  Rows at or past L
+// are zero.
 template <int D>
-__device__ __forceinline__ void stage_rows(const uint16_t* src, int L, int row0, uint16_t (*dst)[D + kPadRow]) {
-    constexpr int kChunks = D / 8;  // 16-byte chunks per row
+struct RowChunks {
+    static constexpr int kChunks = D / 8;                    // 16-byte chunks per row
+    static constexpr int kPer = kRows * kChunks / kThreads;  // chunks per thread
+    u32x4 c[kPer];
+    __device__ __forceinline__ void load(const uint16_t* src, int L, int row0) {
 #pragma unroll
-    for (int j = 0; j < kRows * kChunks / kThreads; ++j) {
-        const int c = threadIdx.x + kThreads * j;
-        const int row = c / kChunks;
-        const int col = (c % kChunks) * 8;
-        u32x4 val = {0u, 0u, 0u, 0u};
-        if (row0 + row < L) val = load16(src + (size_t)(row0 + row) * D + col);
-        *reinterpret_cast<u32x4*>(&dst[row][col]) = val;
-    }
-}
-
-// The same rows transposed: dst[d][row].  Thread t takes the row pair
-// (2 (t % 32), 2 (t % 32) + 1) and D/8 consecutive columns, and writes each
-// column's pair as one 32-bit word.
-template <int D>
-__device__ __forceinline__ void stage_transposed(const uint16_t* src, int L, int row0, uint16_t (*dst)[kPitchT]) {
-    constexpr int kCols = D / 8;           // columns per thread
-    const int kp = threadIdx.x % 32;
-    const int c0 = (threadIdx.x / 32) * kCols;
-    const int ra = row0 + 2 * kp, rb = ra + 1;
-    u32x4 a[kCols / 8], b[kCols / 8];
-#pragma unroll
-    for (int j = 0; j < kCols / 8; ++j) {
-        a[j] = (ra < L) ? load16(src + (size_t)ra * D + c0 + 8 * j) : u32x4{0u, 0u, 0u, 0u};
-        b[j] = (rb < L) ? load16(src + (size_t)rb * D + c0 + 8 * j) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int j = 0; j < kCols / 8; ++j) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t wa = a[j][e / 2], wb = b[j][e / 2];
-            const uint32_t lo = (e & 1) ? (wa >> 16) : (wa & 0xffffu);
-            const uint32_t hi = (e & 1) ? (wb & 0xffff0000u) : (wb << 16);
-            *reinterpret_cast<uint32_t*>(&dst[c0 + 8 * j + e][2 * kp]) = lo | hi;
+        for (int j = 0; j < kPer; ++j) {
+            const int i = threadIdx.x + kThreads * j;
+            const int row = i / kChunks, col = (i % kChunks) * 8;
+            c[j] = (row0 + row < L) ? load16(src + (size_t)(row0 + row) * D + col) : u32x4{0u, 0u, 0u, 0u};
         }
     }
+    __device__ __forceinline__ void store(uint16_t (*dst)[D + kPadRow]) const {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int i = threadIdx.x + kThreads * j;
+            *reinterpret_cast<u32x4*>(&dst[i / kChunks][(i % kChunks) * 8]) = c[j];
+        }
+    }
+};
+
+// The same rows for a transposed LDS tile dst[d][row]: thread t holds the row
+// pair (2 (t % 32), 2 (t % 32) + 1) over D/8 consecutive columns and writes
+// each column's pair as one 32-bit word.
+template <int D>
+struct PairChunks {
+    static constexpr int kCols = D / 8;
+    u32x4 a[kCols / 8], b[kCols / 8];
+    __device__ __forceinline__ void load(const uint16_t* src, int L, int row0) {
+        const int kp = threadIdx.x % 32, c0 = (threadIdx.x / 32) * kCols;
+        const int ra = row0 + 2 * kp, rb = ra + 1;
+#pragma unroll
+        for (int j = 0; j < kCols / 8; ++j) {
+            a[j] = (ra < L) ? load16(src + (size_t)ra * D + c0 + 8 * j) : u32x4{0u, 0u, 0u, 0u};
+            b[j] = (rb < L) ? load16(src + (size_t)rb * D + c0 + 8 * j) : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    // The same rows, row-major (no second global load of the tile).
+    __device__ __forceinline__ void store_rows(uint16_t (*dst)[D + kPadRow]) const {
+        const int kp = threadIdx.x % 32, c0 = (threadIdx.x / 32) * kCols;
+#pragma unroll
+        for (int j = 0; j < kCols / 8; ++j) {
+            *reinterpret_cast<u32x4*>(&dst[2 * kp][c0 + 8 * j]) = a[j];
+            *reinterpret_cast<u32x4*>(&dst[2 * kp + 1][c0 + 8 * j]) = b[j];
+        }
+    }
+    __device__ __forceinline__ void store(uint16_t (*dst)[kPitchT]) const {
+        const int kp = threadIdx.x % 32, c0 = (threadIdx.x / 32) * kCols;
+#pragma unroll
+        for (int j = 0; j < kCols / 8; ++j) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t wa = a[j][e / 2], wb = b[j][e / 2];
+                const uint32_t lo = (e & 1) ? (wa >> 16) : (wa & 0xffffu);
+                const uint32_t hi = (e & 1) ? (wb & 0xffff0000u) : (wb << 16);
+                *reinterpret_cast<uint32_t*>(&dst[c0 + 8 * j + e][2 * kp]) = lo | hi;
+            }
+        }
+    }
+};
+
+template <int D>
+__device__ __forceinline__ void stage_rows(const uint16_t* src, int L, int row0, uint16_t (*dst)[D + kPadRow]) {
+    RowChunks<D> t;
+    t.load(src, L, row0);
+    t.store(dst);
+}
+
+template <int D>
+__device__ __forceinline__ void stage_transposed(const uint16_t* src, int L, int row0, uint16_t (*dst)[kPitchT]) {
+    PairChunks<D> t;
+    t.load(src, L, row0);
+    t.store(dst);
 }
 
 // ------------------------------------------------------------------ forward
@@ -145,11 +182,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd(AttnArgs a) {
 #pragma unroll
     for (int nb = 0; nb < D / 16; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int key0 = 0; key0 < a.lk; key0 += kRows) {
-        __syncthreads();
-        stage_rows<D>(K, a.lk, key0, s.k);
-        stage_transposed<D>(V, a.lk, key0, s.vt);
-        __syncthreads();
+    // Products of one staged 64-key tile.
+    auto tile = [&](int key0) {
 #pragma unroll
         for (int kb = 0; kb < kRows / 16; ++kb) {
             f32x4 st = {0.f, 0.f, 0.f, 0.f};
@@ -180,6 +214,23 @@ __global__ __launch_bounds__(kThreads) void attn_fwd(AttnArgs a) {
                 acc[nb] = mfma16(va, pb, acc[nb]);
             }
         }
+    };
+    // The next tile's global loads are issued before this tile's products,
+    // so they overlap the MFMA work.
+    RowChunks<D> kn;
+    PairChunks<D> vn;
+    kn.load(K, a.lk, 0);
+    vn.load(V, a.lk, 0);
+    for (int key0 = 0; key0 < a.lk; key0 += kRows) {
+        __syncthreads();
+        kn.store(s.k);
+        vn.store(s.vt);
+        __syncthreads();
+        if (key0 + kRows < a.lk) {
+            kn.load(K, a.lk, key0 + kRows);
+            vn.load(V, a.lk, key0 + kRows);
+        }
+        tile(key0);
     }
     const float total = group_sum(lsum);
     if (!qv) return;
@@ -234,12 +285,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq(AttnArgs a) {
 #pragma unroll
     for (int nb = 0; nb < D / 16; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int key0 = 0; key0 < a.lk; key0 += kRows) {
-        __syncthreads();
-        stage_rows<D>(K, a.lk, key0, s.k);
-        stage_transposed<D>(K, a.lk, key0, s.kt);
-        stage_rows<D>(V, a.lk, key0, s.v);
-        __syncthreads();
+    auto tile = [&](int key0) {
 #pragma unroll
         for (int kb = 0; kb < kRows / 16; ++kb) {
             f32x4 st = {0.f, 0.f, 0.f, 0.f}, dpt = {0.f, 0.f, 0.f, 0.f};
@@ -262,6 +308,24 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq(AttnArgs a) {
                 acc[nb] = mfma16(ka, dsb, acc[nb]);
             }
         }
+    };
+    // K is loaded once as row pairs and written both row-major and
+    // transposed; the next tile's loads overlap this tile's products.
+    PairChunks<D> kn;
+    RowChunks<D> vn;
+    kn.load(K, a.lk, 0);
+    vn.load(V, a.lk, 0);
+    for (int key0 = 0; key0 < a.lk; key0 += kRows) {
+        __syncthreads();
+        kn.store_rows(s.k);
+        kn.store(s.kt);
+        vn.store(s.v);
+        __syncthreads();
+        if (key0 + kRows < a.lk) {
+            kn.load(K, a.lk, key0 + kRows);
+            vn.load(V, a.lk, key0 + kRows);
+        }
+        tile(key0);
     }
     if (!qv) return;
     float* dQ = a.dq + bh * a.lq * D + (size_t)q * D;
