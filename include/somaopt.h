@@ -125,6 +125,8 @@ typedef struct {
     int64_t pass1_chunk;        /* max elements per norm-pass workgroup        */
     int64_t pass2_chunk;        /* max elements per update-pass workgroup      */
     int64_t table_bytes;        /* device bytes of the descriptor tables       */
+    int64_t pass1_wg_per_cu;    /* resident norm-pass workgroups per CU (0: no limit)   */
+    int64_t pass2_wg_per_cu;    /* resident update-pass workgroups per CU (0: no limit) */
 } somaopt_plan_info;
 
 /* One row of the host-side plan, for inspection (somaopt_debug_plan). */

@@ -345,33 +345,6 @@ __device__ __forceinline__ float load_g1(const AS_GLOBAL char* gbase, size_t i) 
     else return widen16<GDT>(((const AS_GLOBAL uint16_t*)gbase)[i]);
 }
 
-// Streaming loads and stores carry the nontemporal hint: every byte is used
-// exactly once per step, and on gfx950 the hint raises sustained bandwidth of
-// this 4-read / 3-write stream by about a tenth over plain accesses.
-template <typename T>
-__device__ __forceinline__ T ld_nt(const AS_GLOBAL T* p) {
-    return __builtin_nontemporal_load(p);
-}
-template <typename T>
-__device__ __forceinline__ void st_nt(AS_GLOBAL T* p, const T& v) {
-    __builtin_nontemporal_store(v, p);
-}
-
-template <int GDT>
-__device__ __forceinline__ f32x4 widen_g4(const AS_GLOBAL char* gbase, uint32_t i) {
-    if constexpr (GDT == SOMAOPT_F32) {
-        return ld_nt((const AS_GLOBAL f32x4*)gbase + i);
-    } else {
-        const u32x2 w = ld_nt((const AS_GLOBAL u32x2*)gbase + i);
-        f32x4 r;
-        r.x = widen_lo<GDT>(w.x);
-        r.y = widen_hi<GDT>(w.x);
-        r.z = widen_lo<GDT>(w.y);
-        r.w = widen_hi<GDT>(w.y);
-        return r;
-    }
-}
-
 template <int LDT>
 __device__ __forceinline__ u32x2 narrow4(const f32x4& p) {
     u32x2 r;
@@ -382,15 +355,62 @@ __device__ __forceinline__ u32x2 narrow4(const f32x4& p) {
 
 constexpr int kNoLowp = -1;
 
+// Buffer resource over `bytes` bytes at `base` (raw addressing, stride 0):
+// the hardware bounds-checks every access against the segment, so a load past
+// the end returns zero and a store past it is dropped.  Word 3 selects the
+// 32-bit data format that untyped buffer accesses require on gfx9-family parts.
+constexpr int kRsrcWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t seg_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+// Cache-policy operand of the streaming buffer accesses: nt (nontemporal).
+// Every byte is used exactly once per step; on gfx950 the hint raises the
+// sustained bandwidth of this 4-read / 3-write stream by about a tenth over
+// plain accesses.
+constexpr int kLdPolicy = 2;
+constexpr int kStPolicy = 2;
+
+__device__ __forceinline__ f32x4 bload4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kLdPolicy));
+}
+__device__ __forceinline__ u32x2 bload2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kLdPolicy));
+}
+__device__ __forceinline__ void bstore4(__amdgpu_buffer_rsrc_t r, uint32_t off, const f32x4& x) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, (int)off, 0, kStPolicy);
+}
+__device__ __forceinline__ void bstore2(__amdgpu_buffer_rsrc_t r, uint32_t off, const u32x2& x) {
+    __builtin_amdgcn_raw_buffer_store_b64(x, r, (int)off, 0, kStPolicy);
+}
+
+template <int GDT>
+__device__ __forceinline__ f32x4 widen_g4_buf(__amdgpu_buffer_rsrc_t r, uint32_t i) {
+    if constexpr (GDT == SOMAOPT_F32) {
+        return bload4(r, 16u * i);
+    } else {
+        const u32x2 w = bload2(r, 8u * i);
+        f32x4 x;
+        x.x = widen_lo<GDT>(w.x);
+        x.y = widen_hi<GDT>(w.x);
+        x.z = widen_lo<GDT>(w.y);
+        x.w = widen_hi<GDT>(w.y);
+        return x;
+    }
+}
+
 // One segment of the update pass.  Each thread takes kVecsPerThread vectors
 // spaced BS apart and issues all of their loads before any arithmetic, so a
 // wave keeps 4 x (3 x 16 + 8 or 16) bytes per lane in flight; a segment of at
-// most BS * kVecsPerThread vectors is a single batch.  GDT is the gradient
-// dtype, LDT the working-copy dtype (kNoLowp: none).
+// most BS * kVecsPerThread vectors is a single batch.  The vector body goes
+// through buffer instructions with one resource per array and segment: the
+// addresses are a 32-bit lane offset on a scalar base, and lanes past the end
+// of the body need no branch (their loads read zero, their stores are
+// dropped).  GDT is the gradient dtype, LDT the working-copy dtype (kNoLowp:
+// none).
 template <int BS, int GDT, int LDT>
 __device__ __forceinline__ void update_segment(const Seg2& sg, const GroupConst& c, float scale, int tid) {
     constexpr int U = kVecsPerThread;
-    constexpr size_t kGsz = GDT == SOMAOPT_F32 ? 4 : 2;
+    constexpr uint32_t kGsz = GDT == SOMAOPT_F32 ? 4 : 2;
     AS_GLOBAL float* p = gptr<float>(sg.p);
     AS_GLOBAL float* m = gptr<float>(sg.m);
     AS_GLOBAL float* v = gptr<float>(sg.v);
@@ -406,34 +426,31 @@ __device__ __forceinline__ void update_segment(const Seg2& sg, const GroupConst&
         v[k] = vq;
         if constexpr (LDT != kNoLowp) lp[k] = narrow16<LDT>(pp);
     }
-    AS_GLOBAL f32x4* pv = (AS_GLOBAL f32x4*)(p + sg.head);
-    AS_GLOBAL f32x4* mv = (AS_GLOBAL f32x4*)(m + sg.head);
-    AS_GLOBAL f32x4* vv = (AS_GLOBAL f32x4*)(v + sg.head);
-    AS_GLOBAL u32x2* lv = (AS_GLOBAL u32x2*)(lp + sg.head);
-    const AS_GLOBAL char* gv = gb + sg.head * kGsz;
     const uint32_t nvec = sg.nvec;
-    for (uint32_t i0 = tid; i0 < nvec; i0 += BS * U) {
+    const __amdgpu_buffer_rsrc_t rp = seg_rsrc((const void*)(p + sg.head), 16u * nvec);
+    const __amdgpu_buffer_rsrc_t rm = seg_rsrc((const void*)(m + sg.head), 16u * nvec);
+    const __amdgpu_buffer_rsrc_t rv = seg_rsrc((const void*)(v + sg.head), 16u * nvec);
+    const __amdgpu_buffer_rsrc_t rg = seg_rsrc((const void*)(gb + sg.head * kGsz), 4u * kGsz * nvec);
+    __amdgpu_buffer_rsrc_t rl;
+    if constexpr (LDT != kNoLowp) rl = seg_rsrc((const void*)(lp + sg.head), 8u * nvec);
+    for (uint32_t base = 0; base < nvec; base += BS * U) {
         f32x4 pr[U], mr[U], vr[U], gr[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const uint32_t i = i0 + u * BS;
-            if (i < nvec) {
-                pr[u] = ld_nt(pv + i);
-                mr[u] = ld_nt(mv + i);
-                vr[u] = ld_nt(vv + i);
-                gr[u] = widen_g4<GDT>(gv, i);
-            }
+            const uint32_t i = base + u * BS + tid;
+            pr[u] = bload4(rp, 16u * i);
+            mr[u] = bload4(rm, 16u * i);
+            vr[u] = bload4(rv, 16u * i);
+            gr[u] = widen_g4_buf<GDT>(rg, i);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const uint32_t i = i0 + u * BS;
-            if (i < nvec) {
-                adamw_vec(pr[u], mr[u], vr[u], gr[u], c, scale);
-                st_nt(pv + i, pr[u]);
-                st_nt(mv + i, mr[u]);
-                st_nt(vv + i, vr[u]);
-                if constexpr (LDT != kNoLowp) st_nt(lv + i, narrow4<LDT>(pr[u]));
-            }
+            const uint32_t i = base + u * BS + tid;
+            adamw_vec(pr[u], mr[u], vr[u], gr[u], c, scale);
+            bstore4(rp, 16u * i, pr[u]);
+            bstore4(rm, 16u * i, mr[u]);
+            bstore4(rv, 16u * i, vr[u]);
+            if constexpr (LDT != kNoLowp) bstore2(rl, 8u * i, narrow4<LDT>(pr[u]));
         }
     }
     if ((uint32_t)tid < sg.tail) {
@@ -501,7 +518,7 @@ __global__ void set_step_kernel(DevState* st, int64_t step, int32_t n) {
 }  // namespace
 
 hipError_t launch_pass1(const Pass1Args& a, hipStream_t s) {
-    hipLaunchKernelGGL(sqnorm_pass1<kPass1Threads>, dim3(a.n_blocks), dim3(kPass1Threads), 0, s, a);
+    hipLaunchKernelGGL(sqnorm_pass1<kPass1Threads>, dim3(a.n_blocks), dim3(kPass1Threads), a.lds_bytes, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.n_blocks > kTwoLevelAbove) {
@@ -515,7 +532,7 @@ hipError_t launch_pass1(const Pass1Args& a, hipStream_t s) {
 }
 
 hipError_t launch_pass2(const Pass2Args& a, hipStream_t s) {
-    hipLaunchKernelGGL(adamw_pass2<kPass2Threads>, dim3(a.n_blocks), dim3(kPass2Threads), 0, s, a);
+    hipLaunchKernelGGL(adamw_pass2<kPass2Threads>, dim3(a.n_blocks), dim3(kPass2Threads), a.lds_bytes, s, a);
     return hipGetLastError();
 }
 

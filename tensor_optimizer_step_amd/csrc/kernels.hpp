@@ -14,6 +14,31 @@ constexpr int kFinalizeThreads = 1024;
 // Update pass: 4-element vectors per thread per batch (see update_segment).
 constexpr int kVecsPerThread = 4;
 
+// Resident workgroups per compute unit.  Both streaming passes use no LDS for
+// data; a launch reserves a share of the CU's LDS so that no more than this
+// many workgroups are resident at once.  Measured on MI355X:
+//  - tables of large tensors (a workgroup streams one full segment): the
+//    4-read / 3-write update stream sustains its highest HBM bandwidth with two
+//    256-thread workgroups (8 waves) per CU, about 10% above the unrestricted
+//    occupancy of five, because fewer concurrent streams keep DRAM rows open
+//    longer; the read-only norm pass prefers six (7% faster on 7B-scale state);
+//  - tables of many small tensors (a workgroup walks several short segments,
+//    each starting with dependent descriptor loads): the update pass needs
+//    four per CU to hide those latencies, and the norm pass no limit.
+constexpr int kPass1WgPerCuStreaming = 6;
+constexpr int kPass2WgPerCuStreaming = 2;
+constexpr int kPass2WgPerCuPacked = 4;
+// LDS bytes to reserve per workgroup for `wg_per_cu` resident workgroups on a
+// CU with `lds_per_cu` bytes (2 KiB granules, so that allocation rounding
+// never lowers the count); 0 if the device reports no LDS size.
+inline uint32_t occupancy_lds(int64_t lds_per_cu, int wg_per_cu) {
+    if (lds_per_cu <= 0 || wg_per_cu <= 0) return 0;
+    const int64_t granule = 2048;
+    const int64_t per = (lds_per_cu / wg_per_cu) / granule * granule;
+    const int64_t max_per_wg = 64 * 1024;
+    return (uint32_t)(per > max_per_wg ? max_per_wg : per);
+}
+
 // Norm-pass tables with more partials than this are reduced in two levels:
 // kReduceSpan consecutive partials per workgroup, then the finalize.
 constexpr uint32_t kTwoLevelAbove = 8192;
@@ -29,6 +54,7 @@ struct Pass1Args {
     DevState* state;
     int32_t n_groups;
     int32_t advance;             // 1: this pass opens a new update (t += 1)
+    uint32_t lds_bytes;          // LDS reserved per workgroup (occupancy limit)
 };
 
 struct Pass2Args {
@@ -36,6 +62,7 @@ struct Pass2Args {
     const uint32_t* blk_first;
     uint32_t n_blocks;           // >= 1
     const DevState* state;
+    uint32_t lds_bytes;          // LDS reserved per workgroup (occupancy limit)
 };
 
 hipError_t launch_pass1(const Pass1Args& a, hipStream_t s);

@@ -25,11 +25,11 @@ std::string fmt(const char* f, long long a = 0, long long b = 0, long long c = 0
 
 }  // namespace
 
-int64_t normalise_chunk(int64_t requested, int64_t dflt) {
+int64_t normalise_chunk(int64_t requested, int64_t dflt, int64_t max_chunk) {
     int64_t c = requested > 0 ? requested : dflt;
     c = (c / 8) * 8;
     if (c < 256) c = 256;
-    if (c > (int64_t(1) << 30)) c = int64_t(1) << 30;
+    if (c > max_chunk) c = max_chunk;
     return c;
 }
 
@@ -209,6 +209,15 @@ Plan build_plan(const somaopt_tensor_desc* d, int64_t n, int pass, int64_t chunk
     plan.block_first.push_back((uint32_t)plan.segs.size());
     if (plan.segs.empty()) plan.block_first.assign(1, 0);
     return plan;
+}
+
+bool streaming_plan(const Plan& p) {
+    int64_t total = 0, full = 0;
+    for (const PlanSeg& s : p.segs) {
+        total += s.numel;
+        if (s.numel == p.chunk) full += s.numel;
+    }
+    return total > 0 && 2 * full >= total;
 }
 
 }  // namespace somaopt

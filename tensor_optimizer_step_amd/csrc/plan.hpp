@@ -84,8 +84,17 @@ int validate_host(const somaopt_tensor_desc* d, int64_t n, int32_t n_groups, std
 Plan build_plan(const somaopt_tensor_desc* d, int64_t n, int pass, int64_t chunk,
                 int64_t segment_cost = kSegmentCost);
 
-// Normalise a requested chunk: positive multiple of 8, at least 256 elements.
-int64_t normalise_chunk(int64_t requested, int64_t dflt);
+// Largest update-pass segment: its vector body is addressed with 32-bit byte
+// offsets (16 bytes per 4-element vector) by the buffer instructions.
+constexpr int64_t kMaxPass2Chunk = int64_t(1) << 26;
+
+// Normalise a requested chunk: positive multiple of 8, at least 256 elements,
+// at most `max_chunk`.
+int64_t normalise_chunk(int64_t requested, int64_t dflt, int64_t max_chunk = int64_t(1) << 30);
+
+// True when at least half of the plan's elements lie in segments of the full
+// chunk length, i.e. most workgroups stream one long run of one tensor.
+bool streaming_plan(const Plan& p);
 
 inline int64_t grad_elem_bytes(int32_t dtype) { return dtype == SOMAOPT_F32 ? 4 : 2; }
 

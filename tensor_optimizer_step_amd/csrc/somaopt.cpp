@@ -34,6 +34,8 @@ struct somaopt_handle {
     Seg2* d_seg2 = nullptr;
     uint32_t* d_blk2 = nullptr;
     uint32_t nblk2 = 0;
+    uint32_t lds1 = 0;             // LDS reserved per norm-pass workgroup
+    uint32_t lds2 = 0;             // LDS reserved per update-pass workgroup
     double* d_partials = nullptr;
     double* d_partials2 = nullptr;
     DevState* d_state = nullptr;
@@ -184,6 +186,8 @@ void fill_info(somaopt_plan_info* info, int64_t n_tensors, const Counts& c, cons
     info->pass2_chunk = p2.chunk;
     info->table_bytes = (int64_t)(p1.segs.size() * sizeof(Seg1) + p2.segs.size() * sizeof(Seg2) +
                                   (p1.block_first.size() + p2.block_first.size()) * sizeof(uint32_t));
+    info->pass1_wg_per_cu = streaming_plan(p1) ? kPass1WgPerCuStreaming : 0;
+    info->pass2_wg_per_cu = streaming_plan(p2) ? kPass2WgPerCuStreaming : kPass2WgPerCuPacked;
 }
 
 int launch_norm_pass(somaopt_handle* h, int advance, hipStream_t s) {
@@ -196,6 +200,7 @@ int launch_norm_pass(somaopt_handle* h, int advance, hipStream_t s) {
     a.state = h->d_state;
     a.n_groups = h->n_groups;
     a.advance = advance;
+    a.lds_bytes = h->lds1;
     hipError_t e = launch_pass1(a, s);
     return e == hipSuccess ? SOMAOPT_OK : hip_fail(e, "norm pass launch");
 }
@@ -207,6 +212,7 @@ int launch_update_pass(somaopt_handle* h, hipStream_t s) {
     a.blk_first = h->d_blk2;
     a.n_blocks = h->nblk2;
     a.state = h->d_state;
+    a.lds_bytes = h->lds2;
     hipError_t e = launch_pass2(a, s);
     return e == hipSuccess ? SOMAOPT_OK : hip_fail(e, "update pass launch");
 }
@@ -231,7 +237,7 @@ int64_t somaopt_debug_plan(const somaopt_tensor_desc* descs, int64_t n_tensors, 
     int rc = validate_host(descs, n_tensors, n_groups, err, &c);
     if (rc != SOMAOPT_OK) return fail(rc, err);
     const int64_t ch1 = normalise_chunk(pass1_chunk, kDefaultPass1Chunk);
-    const int64_t ch2 = normalise_chunk(pass2_chunk, kDefaultPass2Chunk);
+    const int64_t ch2 = normalise_chunk(pass2_chunk, kDefaultPass2Chunk, kMaxPass2Chunk);
     Plan p1 = build_plan(descs, n_tensors, 1, ch1);
     Plan p2 = build_plan(descs, n_tensors, 2, ch2);
     if (info) fill_info(info, n_tensors, c, p1, p2);
@@ -272,7 +278,7 @@ int somaopt_init_tensor_table(const somaopt_tensor_desc* descs, int64_t n_tensor
     if ((rc = check_pointers(descs, n_tensors, dev))) return rc;
 
     const int64_t ch1 = normalise_chunk(env_int("SOMAOPT_PASS1_CHUNK", 0), kDefaultPass1Chunk);
-    const int64_t ch2 = normalise_chunk(env_int("SOMAOPT_PASS2_CHUNK", 0), kDefaultPass2Chunk);
+    const int64_t ch2 = normalise_chunk(env_int("SOMAOPT_PASS2_CHUNK", 0), kDefaultPass2Chunk, kMaxPass2Chunk);
     const int64_t seg_cost = std::max<int64_t>(0, env_int("SOMAOPT_SEGMENT_COST", kSegmentCost));
     Plan p1 = build_plan(descs, n_tensors, 1, ch1, seg_cost);
     Plan p2 = build_plan(descs, n_tensors, 2, ch2, seg_cost);
@@ -333,6 +339,14 @@ int somaopt_init_tensor_table(const somaopt_tensor_desc* descs, int64_t n_tensor
     fill_info(&h->info, n_tensors, counts, p1, p2);
     h->nblk1 = (uint32_t)(p1.block_first.size() - 1);
     h->nblk2 = (uint32_t)p2.n_blocks();
+    int lds_per_cu = 0;
+    if ((e = hipDeviceGetAttribute(&lds_per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev)) !=
+        hipSuccess) {
+        free_handle(h);
+        return hip_fail(e, "hipDeviceGetAttribute(LDS per CU)");
+    }
+    h->lds1 = occupancy_lds(lds_per_cu, (int)h->info.pass1_wg_per_cu);
+    h->lds2 = occupancy_lds(lds_per_cu, (int)h->info.pass2_wg_per_cu);
     hipStream_t s = static_cast<hipStream_t>(stream);
 
     if ((e = alloc_upload(&h->d_seg1, s1, s)) != hipSuccess ||

@@ -162,6 +162,24 @@ def test_plan_many_small_tensors_pack_into_few_blocks():
     assert info.pass2_segments == len(sizes)
 
 
+def test_occupancy_follows_the_table_shape():
+    """Large tensors (full-length segments) get the streaming occupancy limits
+    (6 norm-pass and 2 update-pass workgroups per CU); a table of many small
+    tensors, whose workgroups walk several short segments, gets 4 update-pass
+    workgroups per CU and no norm-pass limit."""
+    big = _rows([1 << 20] * 4 + [1024] * 3, dtypes=[S.BF16] * 7)
+    _, info = S.debug_plan(big, 1, 2)
+    assert (info.pass1_wg_per_cu, info.pass2_wg_per_cu) == (6, 2)
+    rng = np.random.default_rng(3)
+    small = _rows([int(x) for x in rng.integers(1, 4097, size=2000)])
+    _, info = S.debug_plan(small, 1, 2)
+    assert (info.pass1_wg_per_cu, info.pass2_wg_per_cu) == (0, 4)
+    # half of the elements in full segments is still a streaming table
+    mixed = _rows([8192 * 8] + [100] * 600)
+    _, info = S.debug_plan(mixed, 1, 2)
+    assert info.pass2_wg_per_cu == 2
+
+
 def test_plan_empty_table():
     segs, info = S.debug_plan([], 1, 2)
     assert segs == [] and info.trainable_numel == 0
