@@ -1,10 +1,9 @@
 /*
  * somaopt.h - fused clip + AdamW optimizer step for AMD Instinct MI355X (gfx950).
  *
- * What the library computes (SomaSpeed landing page, paragraphs "After
- * backward, each trainable tensor has a gradient ..." and "SomaSpeed batches
- * that work across tensors ..."): after backward, over a table of many
- * trainable tensors,
+ * What the library computes (SomaSpeed landing page, prose paragraphs 7 and 8,
+ * numbered in page order after the title: the post-backward optimizer work and
+ * its fused form): after backward, over a table of many trainable tensors,
  *   1. normalize the gradients for the effective batch (divide by D),
  *   2. measure one global L2 norm in which every owned gradient element counts
  *      once,
@@ -20,7 +19,7 @@
  *        p     = p - lr*wd*p - (lr / (1 - beta1^t)) * m / (sqrt(v / (1 - beta2^t)) + eps)
  *      with t the group's update count, 1 on the first update.
  * Gradient buffers are never written and frozen tensors are never read or
- * written (same paragraph).  bf16 and fp16 gradients are widened to fp32 for
+ * written (paragraph 8).  bf16 and fp16 gradients are widened to fp32 for
  * the update, the optimizer state stays fp32, and an optional bf16/fp16
  * working copy of the weights is rewritten from the fp32 master (RLinf page,
  * "Retaining Low-Precision Gradients").
@@ -144,9 +143,9 @@ typedef struct {
 typedef struct somaopt_handle somaopt_handle;
 
 /*
- * Build the device-resident tensor and chunk tables (the batching across
- * tensors of the landing page's "SomaSpeed batches that work across tensors"
- * paragraph) so that each pass is one kernel launch over all tensors.
+ * Build the device-resident tensor and chunk tables (the landing page,
+ * paragraph 8, batches the optimizer work across tensors) so that each pass is
+ * one kernel launch over all tensors.
  *
  *   descs[n_tensors]   tensor table (host memory, copied; may be freed after)
  *   groups[n_groups]   initial per-group hyperparameters, 1..SOMAOPT_MAX_GROUPS
@@ -167,7 +166,10 @@ typedef struct somaopt_handle somaopt_handle;
  * a buffer that is not device memory of the current device or that runs past
  * the end of its allocation (skipped if SOMAOPT_SKIP_POINTER_CHECK=1).
  * Tuning (optional environment): SOMAOPT_PASS1_CHUNK, SOMAOPT_PASS2_CHUNK =
- * maximum elements per workgroup of the norm / update pass.
+ * maximum elements per workgroup of the norm / update pass (the update pass
+ * at most 2^26); SOMAOPT_PASS1_WG_PER_CU, SOMAOPT_PASS2_WG_PER_CU = resident
+ * workgroups per compute unit (0: no limit; unset: chosen from the table
+ * shape, reported in somaopt_plan_info).
  */
 int somaopt_init_tensor_table(const somaopt_tensor_desc* descs, int64_t n_tensors,
                               const somaopt_group* groups, int32_t n_groups,
@@ -175,13 +177,13 @@ int somaopt_init_tensor_table(const somaopt_tensor_desc* descs, int64_t n_tensor
                               void* stream, somaopt_handle** out);
 
 /*
- * Norm pass: one launch over every owned gradient segment, fp64 sum of squares
- * per workgroup, and (in the last workgroup to finish, on the device, no host
- * sync) the fixed-order global sum, the norm, the clip coefficient and each
- * group's bias-corrected constants for the next update (landing page: "It
- * first computes the statistics needed for one global clipping decision,
- * accounting for distributed ownership so that each gradient shard
- * contributes once").
+ * Norm pass: one launch over every owned gradient segment (fp64 sum of
+ * squares per workgroup), then a one-workgroup finalize kernel on the same
+ * stream (no host sync) that adds the partials in a fixed order and derives the
+ * norm, the clip coefficient and each group's bias-corrected constants for the
+ * next update.  Landing page, paragraph 8: the statistics for the single
+ * global clip decision are gathered first, with every gradient shard counted
+ * exactly once under distributed ownership.
  * Calling it again before somaopt_fused_adamw_step recomputes the same
  * statistics for the same pending update (the step count advances once).
  */
@@ -190,8 +192,8 @@ int somaopt_grad_sqnorm(somaopt_handle* h, void* stream);
 /*
  * Update pass: one launch over every trainable segment; reads g, p, m, v and
  * writes p, m, v using the statistics the preceding somaopt_grad_sqnorm left
- * on the device (landing page: "The final update reads the original gradients
- * and applies normalization, clipping, and AdamW together").
+ * on the device.  Landing page, paragraph 8: the last pass works from the
+ * unmodified gradients and does normalization, clipping and AdamW at once.
  * SOMAOPT_E_STATE if no somaopt_grad_sqnorm preceded it since the last update.
  */
 int somaopt_fused_adamw_step(somaopt_handle* h, void* stream);
@@ -243,9 +245,9 @@ int64_t somaopt_debug_plan(const somaopt_tensor_desc* descs, int64_t n_tensors, 
 
 /* ------------------------------------------------------------------------
  * Tiled attention over frozen and trainable keys (SomaSpeed landing page,
- * paragraph "Attention is the connection between the action computation and
- * its context": keys and values are read tile by tile without storing the
- * score matrix, and gradient work for frozen inputs is skipped).
+ * paragraph 5: the action queries read context keys and values in tiles, the
+ * full score matrix is never stored, and inputs that are frozen get no
+ * gradient work).
  *
  * Per (batch b, head h): S = scale * Q K^T, P = softmax over keys, O = P V,
  * LSE = log sum_j exp(S_ij).  Keys [0, lk_frozen) are frozen: the backward

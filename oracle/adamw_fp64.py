@@ -6,12 +6,12 @@ It shares no code with the HIP library: it is the plain definition written out
 in NumPy float64, slow and obviously correct.
 
 What it computes (one optimizer step after backward), following the SomaSpeed
-landing page (paragraphs "After backward, each trainable tensor has a
-gradient ..." and "SomaSpeed batches that work across tensors ..."):
+landing page, prose paragraphs 7 and 8 (numbered in page order after the
+title; they name the post-backward work and its fused form):
 
 1. normalize every trainable gradient for the effective batch (divide by D);
 2. measure one global L2 norm over the normalized gradients, in which every
-   owned element counts once ("each gradient shard contributes once");
+   owned element counts once (every gradient shard enters exactly once);
 3. take one global clipping decision c = min(1, max_norm / (norm + 1e-6)),
    the torch ``clip_grad_norm_`` rule the veRL page calls with max_norm=1.0
    (section 4.2, "Gradient Clipping and Optimizer Step");
@@ -21,7 +21,7 @@ gradient ..." and "SomaSpeed batches that work across tensors ..."):
    converted for the update and optimizer states are kept in fp32).
 
 Gradient buffers are never written, and frozen tensors are never read or
-written (landing page, same paragraph).
+written (landing page, paragraph 8).
 
 Readings where the pages are silent (each also listed in the design notes):
 * AdamW is the textbook decoupled form (Loshchilov & Hutter) in torch's

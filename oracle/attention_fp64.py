@@ -3,13 +3,13 @@
 TEST INFRASTRUCTURE ONLY (tests, smoke check, benchmark CPU baseline).  It
 shares no code with the HIP library.
 
-SomaSpeed landing page, paragraph "Attention is the connection between the
-action computation and its context": queries come from the trainable action
-computation, keys and values identify and carry the context; the kernel reads
-keys and values tile by tile without storing the full score matrix and skips
-gradient work for frozen inputs.  Paragraph "The exact structure depends on
-the model": the context keys/values are frozen (backbone features or a frozen
-prefix) while the action stream may add trainable keys/values.
+SomaSpeed landing page, paragraph 5 (prose paragraphs numbered in page order
+after the title): queries come from the trainable action computation, keys
+and values identify and carry the context; the kernel reads keys and values
+tile by tile, never stores the full score matrix and does no gradient work for
+frozen inputs.  Paragraph 6: the context keys/values are frozen (backbone
+features or a frozen prefix) while the action stream may add trainable
+keys/values.
 
 Reading taken (the pages print no formula): textbook scaled dot-product
 attention per (batch, head), no mask,

@@ -1,10 +1,9 @@
 // Tiled attention over frozen and trainable keys (gfx950, bf16 MFMA, fp32
 // accumulation).
 //
-// SomaSpeed landing page, paragraph "Attention is the connection between the
-// action computation and its context": queries from the trainable action
-// computation read the context keys/values tile by tile, without storing the
-// full score matrix, and gradient work for frozen inputs is skipped.  Here the
+// SomaSpeed landing page, paragraph 5: queries from the trainable action
+// computation read the context keys/values tile by tile, the full score
+// matrix is never stored, and frozen inputs get no gradient work.  Here the
 // first lk_frozen keys of every (batch, head) are frozen: the backward produces
 // dQ for every query and dK/dV only for the trainable keys -- the frozen
 // tiles cost three products per tile (S, dP, dQ) instead of five, and the

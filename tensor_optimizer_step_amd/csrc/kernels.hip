@@ -8,15 +8,14 @@
 // workgroup sums for large tables), so the global sum is bitwise reproducible, and
 // derives the norm, the clip coefficient and each group's bias-corrected
 // constants on the device (no host synchronization).  SomaSpeed landing page,
-// paragraph "SomaSpeed batches that work across tensors ...": statistics for
-// one global clipping decision, each gradient shard counted once.
+// paragraph 8: the statistics for one global clip decision, with every
+// gradient shard counted once.
 //
 // Pass 2 (update pass): a streaming elementwise kernel over every trainable
 // segment that reads g, p, m, v and writes p, m, v in one pass, applying the
 // effective-batch normalization, the clip coefficient and decoupled AdamW
-// together (same paragraph: "The final update reads the original gradients and
-// applies normalization, clipping, and AdamW together").  HBM-bound, so plain
-// fp32 FMA arithmetic, no matrix cores.
+// together from the unmodified gradients (same paragraph).  HBM-bound, so
+// plain fp32 FMA arithmetic, no matrix cores.
 #include <hip/hip_runtime.h>
 
 #include "kernels.hpp"

@@ -1,10 +1,10 @@
 // Host-side tensor-table planner: validation, frozen-tensor removal, alignment
 // analysis and the split of every tensor into workgroup-sized segments.
 //
-// The landing page's fused optimizer batches the norm and update work across
-// tensors instead of launching per tensor (paragraph "SomaSpeed batches that
-// work across tensors ..."); here that batching is a device-resident segment
-// table plus a block table, built once by this planner.
+// The landing page's fused optimizer (paragraph 8) batches the norm and update
+// work across tensors instead of launching per tensor; here that batching is a
+// device-resident segment table plus a block table, built once by this
+// planner.
 #pragma once
 
 #include <cstdint>

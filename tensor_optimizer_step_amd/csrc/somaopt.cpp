@@ -345,6 +345,11 @@ int somaopt_init_tensor_table(const somaopt_tensor_desc* descs, int64_t n_tensor
         free_handle(h);
         return hip_fail(e, "hipDeviceGetAttribute(LDS per CU)");
     }
+    // Overrides for tuning on other parts: 0 lifts the limit, unset keeps the
+    // choice made from the table shape.
+    const int64_t w1 = env_int("SOMAOPT_PASS1_WG_PER_CU", -1), w2 = env_int("SOMAOPT_PASS2_WG_PER_CU", -1);
+    if (w1 >= 0) h->info.pass1_wg_per_cu = std::min<int64_t>(w1, 64);
+    if (w2 >= 0) h->info.pass2_wg_per_cu = std::min<int64_t>(w2, 64);
     h->lds1 = occupancy_lds(lds_per_cu, (int)h->info.pass1_wg_per_cu);
     h->lds2 = occupancy_lds(lds_per_cu, (int)h->info.pass2_wg_per_cu);
     hipStream_t s = static_cast<hipStream_t>(stream);
