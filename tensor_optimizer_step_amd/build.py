@@ -31,6 +31,9 @@ def command(out: str) -> list:
     return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
             "-Wall", "-Wno-unused-function",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # matrix-core accumulators in ordinary VGPRs (no AGPR copies around
+            # the softmax rescale of the attention kernels)
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-I", INCLUDE, "-I", CSRC,
             *[os.path.join(CSRC, s) for s in SOURCES], "-o", out]
 

@@ -13,13 +13,16 @@
 // delta fp32 [B][H][Lq]; dQ fp32 [B][H][Lq][D]; dK, dV fp32 [B][H][Lk-Lf][D].
 //
 // Every workgroup is 4 waves; a wave owns 16 rows (queries, or keys in the
-// dK/dV kernel).  MFMA operand layouts (16 lanes r = lane % 16, 4 groups
-// g = lane / 16): for v_mfma_f32_16x16x32_bf16, lane holds A[r][8g..8g+7] and
-// B[8g..8g+7][r]; for v_mfma_f32_16x16x16_bf16, A[r][4g..4g+3] and
-// B[4g..4g+3][r]; both return C[4g+i][r], i = 0..3.  Computing S^T = K Q^T
-// leaves each lane with four consecutive keys of one query -- exactly the
-// operand P^T needs for O^T = V^T P^T -- so no register shuffles are needed
-// between the two products, and each lane owns one query row's softmax state.
+// dK/dV kernel).  All products are v_mfma_f32_16x16x32_bf16: with 16 lanes
+// r = lane % 16 and 4 groups g = lane / 16, a lane holds A[r][8g..8g+7] and
+// B[8g..8g+7][r] and receives C[4g+i][r], i = 0..3.  Computing S^T = K Q^T
+// leaves each lane with four consecutive keys of one query -- the operand P^T
+// needs for O^T = V^T P^T -- so no register shuffles are needed between the
+// two products, and each lane owns one query row's softmax state.  The second
+// product reduces over two such 16-key blocks at once: a lane's eight B
+// values are its keys 4g..4g+3 of both blocks, and its A operand reads the
+// same eight keys from a transposed LDS tile (the order of the terms inside
+// one product's reduction is free).
 #include <hip/hip_runtime.h>
 
 #include "attention.hpp"
@@ -30,7 +33,6 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kRows = 64;          // rows staged per tile (4 waves x 16)
@@ -43,10 +45,6 @@ constexpr float kLn2 = 0.6931471805599453f;
 __device__ __forceinline__ f32x4 mfma32(const u32x4& a, const u32x4& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
                                                    c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma16(const u32x2& a, const u32x2& b, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b),
-                                                     c, 0, 0, 0);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
@@ -69,23 +67,36 @@ __device__ __forceinline__ float group_max(float x) {
     return x;
 }
 
-__device__ __forceinline__ u32x4 load16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+// Raw buffer resource over one (batch, head) matrix of `rows` x D bf16
+// values: the hardware bounds-checks every access, so rows at or past the end
+// read as zero without a branch (and the compiler keeps exact counts of the
+// loads in flight).  Word 3 selects the 32-bit data format untyped buffer
+// accesses require on gfx9-family parts.
+constexpr int kRsrcWord3 = 0x00020000;
+template <int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t mat_rsrc(const uint16_t* base, int rows) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, rows * D * 2, kRsrcWord3);
+}
+// 16 bytes (8 bf16) of row `row`, starting at column `col`.
+template <int D>
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, int row, int col) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (row * D + col) * 2, 0, 0));
+}
 
 // Rows [row0, row0 + 64) of a [L][D] bf16 matrix, as held by one thread
-// between its global loads and its LDS stores (so the loads of the next tile
-// can be in flight while the current tile is computed).  Rows at or past L
-// are zero.
+// between its global loads and its LDS stores (so the loads of later tiles
+// can be in flight while the current tile is computed).  Each wave reads
+// whole rows: lanes 16 apart take consecutive 16-byte chunks of one row.
 template <int D>
 struct RowChunks {
     static constexpr int kChunks = D / 8;                    // 16-byte chunks per row
     static constexpr int kPer = kRows * kChunks / kThreads;  // chunks per thread
     u32x4 c[kPer];
-    __device__ __forceinline__ void load(const uint16_t* src, int L, int row0) {
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t src, int row0) {
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
             const int i = threadIdx.x + kThreads * j;
-            const int row = i / kChunks, col = (i % kChunks) * 8;
-            c[j] = (row0 + row < L) ? load16(src + (size_t)(row0 + row) * D + col) : u32x4{0u, 0u, 0u, 0u};
+            c[j] = bload16<D>(src, row0 + i / kChunks, (i % kChunks) * 8);
         }
     }
     __device__ __forceinline__ void store(uint16_t (*dst)[D + kPadRow]) const {
@@ -97,58 +108,115 @@ struct RowChunks {
     }
 };
 
-// The same rows for a transposed LDS tile dst[d][row]: thread t holds the row
-// pair (2 (t % 32), 2 (t % 32) + 1) over D/8 consecutive columns and writes
-// each column's pair as one 32-bit word.
+// Transposed tiles t[d][row] hold column d of a 64-row tile as 32 words,
+// word w = rows (2w, 2w + 1).  The word index is XOR-swizzled with
+// (512 / D) * (d / 32): the pair stores of one wave (16 or 8 consecutive
+// 8-column chunks times 4 or 8 row pairs) then hit 64 distinct banks, while
+// reads of four consecutive rows (two words at an even index) stay adjacent
+// and 8-byte aligned.
+template <int D>
+__device__ __forceinline__ int tswz(int d, int word) {
+    return word ^ ((512 / D) * (d >> 5));
+}
+// A operand of a 16x16x32 product from a transposed tile: row d, the four
+// rows starting at k0 and the four starting at k1 (k0, k1 multiples of 4).
+template <int D>
+__device__ __forceinline__ u32x4 tpair(const uint16_t (*t)[kPitchT], int d, int k0, int k1) {
+    const u32x2 lo = *reinterpret_cast<const u32x2*>(&t[d][2 * tswz<D>(d, k0 / 2)]);
+    const u32x2 hi = *reinterpret_cast<const u32x2*>(&t[d][2 * tswz<D>(d, k1 / 2)]);
+    return u32x4{lo.x, lo.y, hi.x, hi.y};
+}
+
+// The same rows for a transposed LDS tile dst[d][row]: a thread holds one
+// 16-byte chunk (8 columns) of a row pair (2p, 2p + 1) and writes each
+// column's pair as one 32-bit word.  Consecutive lanes take consecutive chunks
+// of the same row pair, so every global load instruction reads whole rows.
 template <int D>
 struct PairChunks {
-    static constexpr int kCols = D / 8;
-    u32x4 a[kCols / 8], b[kCols / 8];
-    __device__ __forceinline__ void load(const uint16_t* src, int L, int row0) {
-        const int kp = threadIdx.x % 32, c0 = (threadIdx.x / 32) * kCols;
-        const int ra = row0 + 2 * kp, rb = ra + 1;
+    static constexpr int kChunks = D / 8;
+    static constexpr int kPer = (kRows / 2) * kChunks / kThreads;   // row-pair chunks per thread
+    u32x4 a[kPer], b[kPer];
+    __device__ __forceinline__ static int pair(int j) { return (threadIdx.x + kThreads * j) / kChunks; }
+    __device__ __forceinline__ static int col(int j) { return ((threadIdx.x + kThreads * j) % kChunks) * 8; }
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t src, int row0) {
 #pragma unroll
-        for (int j = 0; j < kCols / 8; ++j) {
-            a[j] = (ra < L) ? load16(src + (size_t)ra * D + c0 + 8 * j) : u32x4{0u, 0u, 0u, 0u};
-            b[j] = (rb < L) ? load16(src + (size_t)rb * D + c0 + 8 * j) : u32x4{0u, 0u, 0u, 0u};
+        for (int j = 0; j < kPer; ++j) {
+            a[j] = bload16<D>(src, row0 + 2 * pair(j), col(j));
+            b[j] = bload16<D>(src, row0 + 2 * pair(j) + 1, col(j));
         }
     }
     // The same rows, row-major (no second global load of the tile).
     __device__ __forceinline__ void store_rows(uint16_t (*dst)[D + kPadRow]) const {
-        const int kp = threadIdx.x % 32, c0 = (threadIdx.x / 32) * kCols;
 #pragma unroll
-        for (int j = 0; j < kCols / 8; ++j) {
-            *reinterpret_cast<u32x4*>(&dst[2 * kp][c0 + 8 * j]) = a[j];
-            *reinterpret_cast<u32x4*>(&dst[2 * kp + 1][c0 + 8 * j]) = b[j];
+        for (int j = 0; j < kPer; ++j) {
+            *reinterpret_cast<u32x4*>(&dst[2 * pair(j)][col(j)]) = a[j];
+            *reinterpret_cast<u32x4*>(&dst[2 * pair(j) + 1][col(j)]) = b[j];
         }
     }
     __device__ __forceinline__ void store(uint16_t (*dst)[kPitchT]) const {
-        const int kp = threadIdx.x % 32, c0 = (threadIdx.x / 32) * kCols;
 #pragma unroll
-        for (int j = 0; j < kCols / 8; ++j) {
+        for (int j = 0; j < kPer; ++j) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const uint32_t wa = a[j][e / 2], wb = b[j][e / 2];
                 const uint32_t lo = (e & 1) ? (wa >> 16) : (wa & 0xffffu);
                 const uint32_t hi = (e & 1) ? (wb & 0xffff0000u) : (wb << 16);
-                *reinterpret_cast<uint32_t*>(&dst[c0 + 8 * j + e][2 * kp]) = lo | hi;
+                const int d = col(j) + e;
+                *reinterpret_cast<uint32_t*>(&dst[d][2 * tswz<D>(d, pair(j))]) = lo | hi;
             }
         }
     }
 };
 
 template <int D>
-__device__ __forceinline__ void stage_rows(const uint16_t* src, int L, int row0, uint16_t (*dst)[D + kPadRow]) {
+__device__ __forceinline__ void stage_rows(__amdgpu_buffer_rsrc_t src, int row0, uint16_t (*dst)[D + kPadRow]) {
     RowChunks<D> t;
-    t.load(src, L, row0);
+    t.load(src, row0);
     t.store(dst);
 }
 
 template <int D>
-__device__ __forceinline__ void stage_transposed(const uint16_t* src, int L, int row0, uint16_t (*dst)[kPitchT]) {
+__device__ __forceinline__ void stage_transposed(__amdgpu_buffer_rsrc_t src, int row0, uint16_t (*dst)[kPitchT]) {
     PairChunks<D> t;
-    t.load(src, L, row0);
+    t.load(src, row0);
     t.store(dst);
+}
+
+// Pipeline over the key tiles of one (batch, head): two register stages, so
+// while tile i is computed from LDS the loads of tiles i + 1 and i + 2 are in
+// flight.  `load(stage, row0)` issues a tile's global loads into a stage,
+// `store(stage)` writes a stage to LDS, `compute(row0)` runs a tile's
+// products from LDS.
+// The loads are unconditional: tiles past the end are outside the buffer
+// resource, so they read zero without touching memory.  Tiles are processed in
+// pairs (an odd last tile is paired with an all-padding tile whose keys the
+// products mask out), so the loop body is straight-line and every path into
+// the loop head has the same loads outstanding: the compiler then waits for
+// just the older stage.
+template <class Stage, class Load, class Store, class Compute>
+__device__ __forceinline__ void two_stage_tiles(int n_rows, Stage& s0, Stage& s1, Load load, Store store,
+                                                Compute compute) {
+    // The scheduling barriers keep each stage's loads together and in program
+    // order (otherwise the two prologue stages interleave and the first
+    // stage's wait would cover both).
+    load(s0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load(s1, kRows);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int row0 = 0; row0 < n_rows; row0 += 2 * kRows) {
+        __syncthreads();
+        store(s0);
+        __syncthreads();
+        load(s0, row0 + 2 * kRows);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(row0);
+        __syncthreads();
+        store(s1);
+        __syncthreads();
+        load(s1, row0 + 3 * kRows);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(row0 + kRows);
+    }
 }
 
 // ------------------------------------------------------------------ forward
@@ -165,72 +233,85 @@ __global__ __launch_bounds__(kThreads) void attn_fwd(AttnArgs a) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
     const size_t bh = (size_t)blockIdx.z * a.heads + blockIdx.y;
-    const uint16_t* Q = static_cast<const uint16_t*>(a.q) + bh * a.lq * D;
-    const uint16_t* K = static_cast<const uint16_t*>(a.k) + bh * a.lk * D;
-    const uint16_t* V = static_cast<const uint16_t*>(a.v) + bh * a.lk * D;
+    const auto Q = mat_rsrc<D>(static_cast<const uint16_t*>(a.q) + bh * a.lq * D, a.lq);
+    const auto K = mat_rsrc<D>(static_cast<const uint16_t*>(a.k) + bh * a.lk * D, a.lk);
+    const auto V = mat_rsrc<D>(static_cast<const uint16_t*>(a.v) + bh * a.lk * D, a.lk);
     const int q = blockIdx.x * kRows + 16 * w + r;
     const bool qv = q < a.lq;
-    // B operand of S^T = K Q^T: Q[q][32 kk + 8 g .. + 7]
+    // B operand of S^T = K Q^T: Q[q][32 kk + 8 g .. + 7] (zero past the last query)
     u32x4 qb[D / 32];
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk)
-        qb[kk] = qv ? load16(Q + (size_t)q * D + 32 * kk + 8 * g) : u32x4{0u, 0u, 0u, 0u};
+    for (int kk = 0; kk < D / 32; ++kk) qb[kk] = bload16<D>(Q, q, 32 * kk + 8 * g);
     const float sc = a.scale * kLog2e;   // scores in log2 units
     float m = -INFINITY, lsum = 0.0f;
     f32x4 acc[D / 16];
 #pragma unroll
     for (int nb = 0; nb < D / 16; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Products of one staged 64-key tile.
+    // Products of one staged 64-key tile: the tile's scores, one max and one
+    // rescale of the accumulator per tile, then O^T += V^T P^T over two
+    // 32-key halves.
     auto tile = [&](int key0) {
+        f32x4 st[kRows / 16];
 #pragma unroll
         for (int kb = 0; kb < kRows / 16; ++kb) {
-            f32x4 st = {0.f, 0.f, 0.f, 0.f};
+            st[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < D / 32; ++kk)
-                st = mfma32(*reinterpret_cast<const u32x4*>(&s.k[16 * kb + r][32 * kk + 8 * g]), qb[kk], st);
-            float x[4];
-            float bm = -INFINITY;
+                st[kb] = mfma32(*reinterpret_cast<const u32x4*>(&s.k[16 * kb + r][32 * kk + 8 * g]), qb[kk], st[kb]);
+        }
+        float bm = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < kRows / 16; ++kb) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int key = key0 + 16 * kb + 4 * g + i;
-                x[i] = key < a.lk ? st[i] * sc : -INFINITY;
-                bm = fmaxf(bm, x[i]);
+                st[kb][i] = key < a.lk ? st[kb][i] * sc : -INFINITY;
+                bm = fmaxf(bm, st[kb][i]);
             }
-            bm = group_max(bm);
-            const float mn = fmaxf(m, bm);
-            const float alpha = exp2f(m - mn);   // m = -inf only before the first key
-            m = mn;
+        }
+        bm = group_max(bm);
+        // The first tile always holds key 0, so mn is finite from then on; a
+        // padding tile (every key masked) leaves m unchanged and alpha = 1.
+        const float mn = fmaxf(m, bm);
+        const float alpha = exp2f(m - mn);
+        m = mn;
+        float ps = 0.0f;
+        u32x2 pb[kRows / 16];
+#pragma unroll
+        for (int kb = 0; kb < kRows / 16; ++kb) {
             float p[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) p[i] = exp2f(x[i] - mn);
-            lsum = lsum * alpha + (p[0] + p[1]) + (p[2] + p[3]);
-            const u32x2 pb = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
+            for (int i = 0; i < 4; ++i) p[i] = exp2f(st[kb][i] - mn);
+            ps += (p[0] + p[1]) + (p[2] + p[3]);
+            pb[kb] = u32x2{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
+        }
+        lsum = lsum * alpha + ps;
 #pragma unroll
-            for (int nb = 0; nb < D / 16; ++nb) {
-                acc[nb] *= alpha;
-                const u32x2 va = *reinterpret_cast<const u32x2*>(&s.vt[16 * nb + r][16 * kb + 4 * g]);
-                acc[nb] = mfma16(va, pb, acc[nb]);
-            }
+        for (int nb = 0; nb < D / 16; ++nb) acc[nb] *= alpha;
+#pragma unroll
+        for (int h = 0; h < kRows / 32; ++h) {
+            const u32x4 bop = {pb[2 * h].x, pb[2 * h].y, pb[2 * h + 1].x, pb[2 * h + 1].y};
+#pragma unroll
+            for (int nb = 0; nb < D / 16; ++nb)
+                acc[nb] = mfma32(tpair<D>(s.vt, 16 * nb + r, 32 * h + 4 * g, 32 * h + 16 + 4 * g), bop, acc[nb]);
         }
     };
-    // The next tile's global loads are issued before this tile's products,
-    // so they overlap the MFMA work.
-    RowChunks<D> kn;
-    PairChunks<D> vn;
-    kn.load(K, a.lk, 0);
-    vn.load(V, a.lk, 0);
-    for (int key0 = 0; key0 < a.lk; key0 += kRows) {
-        __syncthreads();
-        kn.store(s.k);
-        vn.store(s.vt);
-        __syncthreads();
-        if (key0 + kRows < a.lk) {
-            kn.load(K, a.lk, key0 + kRows);
-            vn.load(V, a.lk, key0 + kRows);
-        }
-        tile(key0);
-    }
+    struct KV {
+        RowChunks<D> k;
+        PairChunks<D> v;
+    } st0, st1;
+    two_stage_tiles(
+        a.lk, st0, st1,
+        [&](KV& x, int row0) {
+            x.k.load(K, row0);
+            x.v.load(V, row0);
+        },
+        [&](const KV& x) {
+            x.k.store(s.k);
+            x.v.store(s.vt);
+        },
+        tile);
     const float total = group_sum(lsum);
     if (!qv) return;
     const float inv = 1.0f / total;
@@ -258,21 +339,20 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq(AttnArgs a) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
     const size_t bh = (size_t)blockIdx.z * a.heads + blockIdx.y;
-    const uint16_t* Q = static_cast<const uint16_t*>(a.q) + bh * a.lq * D;
-    const uint16_t* dO = static_cast<const uint16_t*>(a.d_o) + bh * a.lq * D;
-    const uint16_t* O = static_cast<const uint16_t*>(a.o) + bh * a.lq * D;
-    const uint16_t* K = static_cast<const uint16_t*>(a.k) + bh * a.lk * D;
-    const uint16_t* V = static_cast<const uint16_t*>(a.v) + bh * a.lk * D;
+    const auto Q = mat_rsrc<D>(static_cast<const uint16_t*>(a.q) + bh * a.lq * D, a.lq);
+    const auto dO = mat_rsrc<D>(static_cast<const uint16_t*>(a.d_o) + bh * a.lq * D, a.lq);
+    const auto O = mat_rsrc<D>(static_cast<const uint16_t*>(a.o) + bh * a.lq * D, a.lq);
+    const auto K = mat_rsrc<D>(static_cast<const uint16_t*>(a.k) + bh * a.lk * D, a.lk);
+    const auto V = mat_rsrc<D>(static_cast<const uint16_t*>(a.v) + bh * a.lk * D, a.lk);
     const int q = blockIdx.x * kRows + 16 * w + r;
     const bool qv = q < a.lq;
     u32x4 qb[D / 32], db[D / 32];
     float dot = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
-        const size_t off = (size_t)q * D + 32 * kk + 8 * g;
-        qb[kk] = qv ? load16(Q + off) : u32x4{0u, 0u, 0u, 0u};
-        db[kk] = qv ? load16(dO + off) : u32x4{0u, 0u, 0u, 0u};
-        const u32x4 ov = qv ? load16(O + off) : u32x4{0u, 0u, 0u, 0u};
+        qb[kk] = bload16<D>(Q, q, 32 * kk + 8 * g);
+        db[kk] = bload16<D>(dO, q, 32 * kk + 8 * g);
+        const u32x4 ov = bload16<D>(O, q, 32 * kk + 8 * g);
 #pragma unroll
         for (int e = 0; e < 8; ++e) dot += bf16_at(db[kk][e / 2], e & 1) * bf16_at(ov[e / 2], e & 1);
     }
@@ -285,6 +365,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq(AttnArgs a) {
     for (int nb = 0; nb < D / 16; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     auto tile = [&](int key0) {
+        u32x2 dsb[kRows / 16];
 #pragma unroll
         for (int kb = 0; kb < kRows / 16; ++kb) {
             f32x4 st = {0.f, 0.f, 0.f, 0.f}, dpt = {0.f, 0.f, 0.f, 0.f};
@@ -300,32 +381,34 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq(AttnArgs a) {
                 const float p = key < a.lk ? exp2f(st[i] * sc - lse2) : 0.0f;
                 ds[i] = p * (dpt[i] - delta);
             }
-            const u32x2 dsb = {pack_bf16(ds[0], ds[1]), pack_bf16(ds[2], ds[3])};
+            dsb[kb] = u32x2{pack_bf16(ds[0], ds[1]), pack_bf16(ds[2], ds[3])};
+        }
+        // dQ^T += K^T dS^T over two 32-key halves
 #pragma unroll
-            for (int nb = 0; nb < D / 16; ++nb) {
-                const u32x2 ka = *reinterpret_cast<const u32x2*>(&s.kt[16 * nb + r][16 * kb + 4 * g]);
-                acc[nb] = mfma16(ka, dsb, acc[nb]);
-            }
+        for (int h = 0; h < kRows / 32; ++h) {
+            const u32x4 bop = {dsb[2 * h].x, dsb[2 * h].y, dsb[2 * h + 1].x, dsb[2 * h + 1].y};
+#pragma unroll
+            for (int nb = 0; nb < D / 16; ++nb)
+                acc[nb] = mfma32(tpair<D>(s.kt, 16 * nb + r, 32 * h + 4 * g, 32 * h + 16 + 4 * g), bop, acc[nb]);
         }
     };
-    // K is loaded once as row pairs and written both row-major and
-    // transposed; the next tile's loads overlap this tile's products.
-    PairChunks<D> kn;
-    RowChunks<D> vn;
-    kn.load(K, a.lk, 0);
-    vn.load(V, a.lk, 0);
-    for (int key0 = 0; key0 < a.lk; key0 += kRows) {
-        __syncthreads();
-        kn.store_rows(s.k);
-        kn.store(s.kt);
-        vn.store(s.v);
-        __syncthreads();
-        if (key0 + kRows < a.lk) {
-            kn.load(K, a.lk, key0 + kRows);
-            vn.load(V, a.lk, key0 + kRows);
-        }
-        tile(key0);
-    }
+    // K is loaded once as row pairs and written both row-major and transposed.
+    struct KV {
+        PairChunks<D> k;
+        RowChunks<D> v;
+    } st0, st1;
+    two_stage_tiles(
+        a.lk, st0, st1,
+        [&](KV& x, int row0) {
+            x.k.load(K, row0);
+            x.v.load(V, row0);
+        },
+        [&](const KV& x) {
+            x.k.store_rows(s.k);
+            x.k.store(s.kt);
+            x.v.store(s.v);
+        },
+        tile);
     if (!qv) return;
     float* dQ = a.dq + bh * a.lq * D + (size_t)q * D;
 #pragma unroll
@@ -351,20 +434,19 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv(AttnArgs a) {
     const int r = lane & 15, g = lane >> 4;
     const size_t bh = (size_t)blockIdx.z * a.heads + blockIdx.y;
     const int lt = a.lk - a.lk_frozen;
-    const uint16_t* Q = static_cast<const uint16_t*>(a.q) + bh * a.lq * D;
-    const uint16_t* dO = static_cast<const uint16_t*>(a.d_o) + bh * a.lq * D;
-    const uint16_t* K = static_cast<const uint16_t*>(a.k) + bh * a.lk * D;
-    const uint16_t* V = static_cast<const uint16_t*>(a.v) + bh * a.lk * D;
+    const auto Q = mat_rsrc<D>(static_cast<const uint16_t*>(a.q) + bh * a.lq * D, a.lq);
+    const auto dO = mat_rsrc<D>(static_cast<const uint16_t*>(a.d_o) + bh * a.lq * D, a.lq);
+    const auto K = mat_rsrc<D>(static_cast<const uint16_t*>(a.k) + bh * a.lk * D, a.lk);
+    const auto V = mat_rsrc<D>(static_cast<const uint16_t*>(a.v) + bh * a.lk * D, a.lk);
     const int j = blockIdx.x * kRows + 16 * w + r;   // trainable key index
     const bool kv = j < lt;
     const int key = a.lk_frozen + j;
-    // B operands: K[key][32 kk + 8 g ..], V[key][32 kk + 8 g ..]
+    // B operands: K[key][32 kk + 8 g ..], V[key][32 kk + 8 g ..] (zero past the last key)
     u32x4 kb_[D / 32], vb_[D / 32];
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
-        const size_t off = (size_t)key * D + 32 * kk + 8 * g;
-        kb_[kk] = kv ? load16(K + off) : u32x4{0u, 0u, 0u, 0u};
-        vb_[kk] = kv ? load16(V + off) : u32x4{0u, 0u, 0u, 0u};
+        kb_[kk] = bload16<D>(K, key, 32 * kk + 8 * g);
+        vb_[kk] = bload16<D>(V, key, 32 * kk + 8 * g);
     }
     const float sc = a.scale * kLog2e;
     f32x4 dk[D / 16], dv[D / 16];
@@ -373,16 +455,17 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv(AttnArgs a) {
 
     for (int q0 = 0; q0 < a.lq; q0 += kRows) {
         __syncthreads();
-        stage_rows<D>(Q, a.lq, q0, s.q);
-        stage_rows<D>(dO, a.lq, q0, s.d_o);
-        stage_transposed<D>(Q, a.lq, q0, s.qt);
-        stage_transposed<D>(dO, a.lq, q0, s.dot);
+        stage_rows<D>(Q, q0, s.q);
+        stage_rows<D>(dO, q0, s.d_o);
+        stage_transposed<D>(Q, q0, s.qt);
+        stage_transposed<D>(dO, q0, s.dot);
         if (threadIdx.x < kRows) {
             const int qq = q0 + threadIdx.x;
             s.lse2[threadIdx.x] = qq < a.lq ? a.lse[bh * a.lq + qq] * kLog2e : INFINITY;
             s.delta[threadIdx.x] = qq < a.lq ? a.delta[bh * a.lq + qq] : 0.0f;
         }
         __syncthreads();
+        u32x2 pb[kRows / 16], dsb[kRows / 16];
 #pragma unroll
         for (int qb = 0; qb < kRows / 16; ++qb) {
             // S = Q K^T and dP = dO V^T: lane holds [query 16 qb + 4 g + i][key r]
@@ -399,14 +482,19 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv(AttnArgs a) {
                 p[i] = exp2f(st[i] * sc - s.lse2[qi]);
                 ds[i] = p[i] * (dpt[i] - s.delta[qi]);
             }
-            const u32x2 pb = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
-            const u32x2 dsb = {pack_bf16(ds[0], ds[1]), pack_bf16(ds[2], ds[3])};
+            pb[qb] = u32x2{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
+            dsb[qb] = u32x2{pack_bf16(ds[0], ds[1]), pack_bf16(ds[2], ds[3])};
+        }
+        // dV^T += dO^T P and dK^T += Q^T dS over two 32-query halves
+#pragma unroll
+        for (int h = 0; h < kRows / 32; ++h) {
+            const u32x4 pop = {pb[2 * h].x, pb[2 * h].y, pb[2 * h + 1].x, pb[2 * h + 1].y};
+            const u32x4 dop = {dsb[2 * h].x, dsb[2 * h].y, dsb[2 * h + 1].x, dsb[2 * h + 1].y};
 #pragma unroll
             for (int nb = 0; nb < D / 16; ++nb) {
-                const u32x2 da = *reinterpret_cast<const u32x2*>(&s.dot[16 * nb + r][16 * qb + 4 * g]);
-                const u32x2 qa = *reinterpret_cast<const u32x2*>(&s.qt[16 * nb + r][16 * qb + 4 * g]);
-                dv[nb] = mfma16(da, pb, dv[nb]);    // dV^T += dO^T P
-                dk[nb] = mfma16(qa, dsb, dk[nb]);   // dK^T += Q^T dS
+                const int k0 = 32 * h + 4 * g, k1 = 32 * h + 16 + 4 * g;
+                dv[nb] = mfma32(tpair<D>(s.dot, 16 * nb + r, k0, k1), pop, dv[nb]);
+                dk[nb] = mfma32(tpair<D>(s.qt, 16 * nb + r, k0, k1), dop, dk[nb]);
             }
         }
     }
