@@ -189,75 +189,117 @@ def sharded_setup(torch, somaopt, W, dev, stream, lowp_dtype):
     return wl, opt, (bufs, views, lowp)
 
 
-ATTN_SHAPE = dict(batch=64, heads=8, lq=64, lk=1024, lk_frozen=960, head_dim=128)
+ATTN_SHAPE = dict(batch=64, heads=8, lq=64, l_ctx=960, l_act=64, head_dim=128)
 
 
 def attention_bench(torch, args):
-    """Tiled attention with a frozen context prefix (one JSON line).
+    """Tiled attention over a frozen context plus trainable action keys (one JSON line).
 
-    Action-token queries (64) attend to 960 frozen context keys plus 64
-    trainable action keys per (batch, head); 64 x 8 heads of dimension 128.
-    Times the forward and the backward (dQ for all queries, dK/dV only for the
-    trainable keys), and the backward with every key trainable for contrast.
+    Per (batch, head): 64 action-token queries attend to 960 frozen context keys
+    (their own buffer, no gradient) and 64 trainable action keys (dK, dV
+    returned); 64 x 8 heads of dimension 128.  Times the forward and the
+    backward; for contrast also the backward with every key trainable, the
+    same forward with one context shared by 4 consecutive query batches (flow
+    timesteps), and the single-buffer entry point on the same keys.
+
+    Four independent input sets (about 1.3 GB) are used in turn, so no call
+    finds its keys and values in the 256 MB last-level cache from the
+    previous call.  Every entry point is first called once with its pointer
+    validation; the timed loops then run back to back with the per-call host
+    validation skipped, so the times are the kernels' own.
     """
     import math
     from tensor_optimizer_step_amd import somaopt
     somaopt.load()
     sh = ATTN_SHAPE
-    b, h, lq, lk, lf, d = (sh[k] for k in ("batch", "heads", "lq", "lk", "lk_frozen", "head_dim"))
+    b, h, lq, lc, la, d = (sh[k] for k in ("batch", "heads", "lq", "l_ctx", "l_act", "head_dim"))
+    lk = lc + la
+    n_sets, share = 4, 4
     gen = torch.Generator(device="cuda")
     gen.manual_seed(4000)
     mk = lambda *x: torch.randn(*x, generator=gen, device="cuda").to(torch.bfloat16)
-    q, k, v, do = mk(b, h, lq, d), mk(b, h, lk, d), mk(b, h, lk, d), mk(b, h, lq, d)
-    o = torch.empty_like(q)
-    lse = torch.empty(b, h, lq, device="cuda")
-    dq = torch.empty(b, h, lq, d, device="cuda")
-    delta = torch.empty(b, h, lq, device="cuda")
-    dk_all = torch.empty(b, h, lk, d, device="cuda")
-    dv_all = torch.empty(b, h, lk, d, device="cuda")
-    dk, dv = dk_all[:, :, : lk - lf].contiguous(), dv_all[:, :, : lk - lf].contiguous()
+    sets = []
+    for _ in range(n_sets):
+        t = dict(q=mk(b, h, lq, d), do=mk(b, h, lq, d), kc=mk(b, h, lc, d), vc=mk(b, h, lc, d),
+                 ka=mk(b, h, la, d), va=mk(b, h, la, d))
+        t.update(o=torch.empty_like(t["q"]), lse=torch.empty(b, h, lq, device="cuda"),
+                 dq=torch.empty(b, h, lq, d, device="cuda"), delta=torch.empty(b, h, lq, device="cuda"),
+                 dk=torch.empty(b, h, la, d, device="cuda"), dv=torch.empty(b, h, la, d, device="cuda"))
+        sets.append(t)
+    s0 = sets[0]
+    kcat, vcat = torch.cat([s0["kc"], s0["ka"]], dim=2).contiguous(), torch.cat([s0["vc"], s0["va"]], dim=2).contiguous()
+    dk_all, dv_all = torch.empty(b, h, lk, d, device="cuda"), torch.empty(b, h, lk, d, device="cuda")
     scale = 1.0 / math.sqrt(d)
     stream = torch.cuda.current_stream()
 
+    def fwd(t):
+        somaopt.attn_ctx_forward(t["q"], t["kc"], t["vc"], t["ka"], t["va"], t["o"], t["lse"], 1, scale, stream)
+
+    def bwd(t):
+        somaopt.attn_ctx_backward(t["q"], t["kc"], t["vc"], t["ka"], t["va"], t["o"], t["lse"], t["do"], t["dq"],
+                                  t["dk"], t["dv"], t["delta"], 1, scale, stream)
+
+    def fwd_shared(t):   # the first batch / 4 context batches, each read by 4 query batches
+        somaopt.attn_ctx_forward(t["q"], t["kc"][: b // share], t["vc"][: b // share], t["ka"], t["va"], t["o"],
+                                 t["lse"], share, scale, stream)
+
+    def fwd_one(_t):
+        somaopt.attn_forward(s0["q"], kcat, vcat, s0["o"], s0["lse"], lc, scale, stream)
+
+    def bwd_all(_t):
+        somaopt.attn_backward(s0["q"], kcat, vcat, s0["o"], s0["lse"], s0["do"], s0["dq"], dk_all, dv_all,
+                              s0["delta"], 0, scale, stream)
+
     def timed(fn, reps):
-        for _ in range(max(args.warmup, 1)):
-            fn()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for t in sets:
+            fn(t)      # validated call
         torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(reps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
+        os.environ["SOMAOPT_SKIP_POINTER_CHECK"] = "1"
+        try:
+            for i in range(max(args.warmup, 1)):
+                fn(sets[i % n_sets])
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for i in range(reps):
+                fn(sets[i % n_sets])
+            e1.record(stream)
+            torch.cuda.synchronize()
+        finally:
+            del os.environ["SOMAOPT_SKIP_POINTER_CHECK"]
         return e0.elapsed_time(e1) / reps
 
-    fwd = lambda: somaopt.attn_forward(q, k, v, o, lse, lf, scale, stream)
-    bwd = lambda: somaopt.attn_backward(q, k, v, o, lse, do, dq, dk, dv, delta, lf, scale, stream)
-    bwd_all = lambda: somaopt.attn_backward(q, k, v, o, lse, do, dq, dk_all, dv_all, delta, 0, scale, stream)
     t0 = time.perf_counter()
     ms_f = timed(fwd, args.steps)
     ms_b = timed(bwd, args.steps)
+    ms_fs = timed(fwd_shared, args.steps)
+    ms_f1 = timed(fwd_one, args.steps)
     ms_ball = timed(bwd_all, args.steps)
     wall = time.perf_counter() - t0
-    bh, lt = b * h, lk - lf
-    bytes_f = bh * (2 * lq * d * 2 + 2 * lk * d * 2) + bh * lq * 4
+    bh = b * h
+    bytes_f = bh * (2 * lq * d * 2 + 2 * lk * d * 2) + bh * lq * 4          # q, o; k, v; lse
+    bytes_fs = bh * (2 * lq * d * 2 + 2 * la * d * 2) + bh // share * 2 * lc * d * 2 + bh * lq * 4
     # minimum traffic: every input read once, every output written once
     bytes_b = bh * (3 * lq * d * 2 + 2 * lq * 4 + 2 * lk * d * 2   # q, dO, o, lse; k, v
-                    + lq * d * 4 + lq * 4                           # dq, delta
-                    + 2 * lt * d * 4)                               # dk, dv (trainable keys)
+                    + lq * d * 4 + lq * 4                          # dq, delta
+                    + 2 * la * d * 4)                              # dk, dv (trainable keys)
     flops_f = 4.0 * bh * lq * lk * d
-    flops_b = bh * (6.0 * lq * lk * d + 4.0 * lq * lt * d)       # S, dP, dQ over all keys; dK, dV over trainable
+    flops_b = bh * (6.0 * lq * lk * d + 4.0 * lq * la * d)       # S, dP, dQ over all keys; dK, dV over trainable
     flops_ball = bh * (6.0 * lq * lk * d + 4.0 * lq * lk * d)
     out = {
         "metric": "tiled attention with a frozen context: forward + backward time (us) and achieved HBM GB/s",
         "value": (ms_f + ms_b) * 1e3, "unit": "us per forward+backward", "higher_is_better": False,
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "data": "synthetic", "dtype": "bf16",
-        "config": {"workload": "frozen_attention", **sh},
+        "config": {"workload": "frozen_attention", **sh, "input_sets": n_sets},
         "forward": {"ms": ms_f, "GBps": bytes_f / ms_f / 1e6, "TFLOPs": flops_f / ms_f / 1e9,
                     "algorithmic_bytes": bytes_f},
         "backward": {"ms": ms_b, "GBps": bytes_b / ms_b / 1e6, "TFLOPs": flops_b / ms_b / 1e9,
                      "algorithmic_bytes": bytes_b},
-        "backward_all_keys_trainable": {"ms": ms_ball, "TFLOPs": flops_ball / ms_ball / 1e9},
+        "forward_context_shared_by_4": {"ms": ms_fs, "GBps": bytes_fs / ms_fs / 1e6,
+                                        "algorithmic_bytes": bytes_fs},
+        "forward_single_buffer_same_keys": {"ms": ms_f1, "note": "one input set (cache-warm)"},
+        "backward_all_keys_trainable": {"ms": ms_ball, "TFLOPs": flops_ball / ms_ball / 1e9,
+                                        "note": "one input set"},
         "roofline": {"bound": "hbm", "achieved": round(bytes_f / ms_f / 1e6, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(bytes_f / ms_f / 1e6 / HBM_PEAK_GBS, 4), "traffic": None,
                      "kernel": "attn_fwd"},

@@ -259,7 +259,7 @@ int64_t somaopt_debug_plan(const somaopt_tensor_desc* descs, int64_t n_tensors, 
  *   dq          fp32 [batch][heads][lq][head_dim]
  *   dk, dv      fp32 [batch][heads][lk - lk_frozen][head_dim] (NULL allowed
  *               when lk_frozen == lk)
- * head_dim is 64 or 128; batch, heads <= 65535; lq, lk >= 1.  Products use
+ * head_dim is 64 or 128; batch, heads <= 65535; lq, lk in [1, 2^22].  Products use
  * bf16 matrix-core inputs (P and dS rounded once to bf16) with fp32
  * accumulation.  Device pointers are caller-owned; the calls only enqueue
  * work on `stream`.  SOMAOPT_E_INVALID on a bad shape, a NULL or misaligned
@@ -284,6 +284,53 @@ int somaopt_attn_forward(const void* q, const void* k, const void* v, void* o, f
 int somaopt_attn_backward(const void* q, const void* k, const void* v, const void* o,
                           const float* lse, const void* d_o, float* dq, float* dk, float* dv,
                           float* delta, const somaopt_attn_shape* shape, void* stream);
+
+/* ------------------------------------------------------------------------
+ * The same attention with the keys split into two separate buffers, covering
+ * the context structures of the landing page's paragraph 6 without copying
+ * any key or value:
+ *   - a frozen context (backbone features or a frozen prefix) shared by
+ *     ctx_share consecutive query batches -- e.g. the sampled flow timesteps
+ *     of one observation -- with no dK/dV;
+ *   - trainable action keys/values, one set per query batch, whose dK/dV are
+ *     returned.
+ * Either part may be empty: l_act = 0 is cross-attention to frozen features
+ * only, l_ctx = 0 is self-attention over trainable keys only.  For query
+ * batch b the keys are context batch b / ctx_share followed by action batch
+ * b; softmax runs over all of them.
+ * Layout (row-major, rows contiguous, base pointers 16-byte aligned):
+ *   q, o, d_o      bf16 [batch][heads][lq][head_dim]
+ *   k_ctx, v_ctx   bf16 [batch / ctx_share][heads][l_ctx][head_dim] (NULL allowed if l_ctx == 0)
+ *   k_act, v_act   bf16 [batch][heads][l_act][head_dim]             (NULL allowed if l_act == 0)
+ *   lse, delta     fp32 [batch][heads][lq]
+ *   dq             fp32 [batch][heads][lq][head_dim]
+ *   dk_act, dv_act fp32 [batch][heads][l_act][head_dim]             (NULL allowed if l_act == 0)
+ * Limits: head_dim 64 or 128; batch, heads <= 65535; lq in [1, 2^22];
+ * l_ctx, l_act in [0, 2^22] with l_ctx + l_act >= 1; ctx_share >= 1 divides
+ * batch.  Numerics, ownership and errors as for somaopt_attn_forward.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+    int32_t batch;       /* query batches                                            */
+    int32_t heads;
+    int32_t lq;          /* queries per (batch, head)                                */
+    int32_t l_ctx;       /* frozen context keys per (context batch, head)            */
+    int32_t l_act;       /* trainable action keys per (batch, head)                  */
+    int32_t ctx_share;   /* consecutive query batches reading one context batch      */
+    int32_t head_dim;    /* 64 or 128                                                */
+    float scale;         /* score scale, usually 1 / sqrt(head_dim)                  */
+} somaopt_attn_ctx_shape;
+
+/* Forward: writes O (bf16) and LSE (fp32, natural log). */
+int somaopt_attn_ctx_forward(const void* q, const void* k_ctx, const void* v_ctx, const void* k_act,
+                             const void* v_act, void* o, float* lse, const somaopt_attn_ctx_shape* shape,
+                             void* stream);
+
+/* Backward from the saved O and LSE: writes dQ, and dK, dV of the action
+ * keys; `delta` is a caller-provided fp32 [batch][heads][lq] workspace. */
+int somaopt_attn_ctx_backward(const void* q, const void* k_ctx, const void* v_ctx, const void* k_act,
+                              const void* v_act, const void* o, const float* lse, const void* d_o, float* dq,
+                              float* dk_act, float* dv_act, float* delta, const somaopt_attn_ctx_shape* shape,
+                              void* stream);
 
 /* Release the handle's device tables, graph and private stream.  Waits for
  * work the handle enqueued.  NULL is ignored. */

@@ -34,11 +34,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRows = 64;          // rows staged per tile (4 waves x 16)
 constexpr int kThreads = 256;
-constexpr int kPadRow = 8;         // bf16 padding of a row-major LDS row
-constexpr int kPitchT = kRows + 4; // bf16 pitch of a transposed LDS row (8-byte aligned reads)
+constexpr int kPadRow = 8;         // bf16 padding of a row-major LDS row read by rows
+constexpr int kPadTr = 16;         // bf16 padding of a row-major LDS row read transposed
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -54,6 +55,10 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 __device__ __forceinline__ float bf16_at(uint32_t w, int half) {
     return __uint_as_float(half ? (w & 0xffff0000u) : (w << 16));
 }
+
+// 2^x with the hardware v_exp_f32: results below 2^-126 flush to zero, which
+// is immaterial for softmax weights (every argument here is <= 0 or -inf).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Sum / max over the four lanes r, r+16, r+32, r+48 that share a row.
 __device__ __forceinline__ float group_sum(float x) {
@@ -99,7 +104,8 @@ struct RowChunks {
             c[j] = bload16<D>(src, row0 + i / kChunks, (i % kChunks) * 8);
         }
     }
-    __device__ __forceinline__ void store(uint16_t (*dst)[D + kPadRow]) const {
+    template <int P>
+    __device__ __forceinline__ void store(uint16_t (*dst)[P]) const {
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
             const int i = threadIdx.x + kThreads * j;
@@ -108,123 +114,95 @@ struct RowChunks {
     }
 };
 
-// Transposed tiles t[d][row] hold column d of a 64-row tile as 32 words,
-// word w = rows (2w, 2w + 1).  The word index is XOR-swizzled with
-// (512 / D) * (d / 32): the pair stores of one wave (16 or 8 consecutive
-// 8-column chunks times 4 or 8 row pairs) then hit 64 distinct banks, while
-// reads of four consecutive rows (two words at an even index) stay adjacent
-// and 8-byte aligned.
-template <int D>
-__device__ __forceinline__ int tswz(int d, int word) {
-    return word ^ ((512 / D) * (d >> 5));
+// Transposed read of a row-major LDS tile with gfx950's ds_read_b64_tr_b16:
+// within each 16-lane group, lane m supplies the address of columns
+// d0 + 4 (m % 4) .. + 3 of row k0 + m / 4, and lane r receives rows
+// k0 .. k0 + 3 of column d0 + r (four bf16 in row order) -- the operand layout
+// of a product that reduces over the rows.  With a row pitch of D + 16 bf16 the
+// 64 lanes' reads are spread evenly over the LDS banks.
+template <int P>
+__device__ __forceinline__ u32x2 tr_rows4(const uint16_t (*t)[P], int k0, int d0, int r) {
+    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+    const uint16_t* p = &t[k0 + (r >> 2)][d0 + 4 * (r & 3)];
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p));
 }
-// A operand of a 16x16x32 product from a transposed tile: row d, the four
-// rows starting at k0 and the four starting at k1 (k0, k1 multiples of 4).
-template <int D>
-__device__ __forceinline__ u32x4 tpair(const uint16_t (*t)[kPitchT], int d, int k0, int k1) {
-    const u32x2 lo = *reinterpret_cast<const u32x2*>(&t[d][2 * tswz<D>(d, k0 / 2)]);
-    const u32x2 hi = *reinterpret_cast<const u32x2*>(&t[d][2 * tswz<D>(d, k1 / 2)]);
+// A operand of a 16x16x32 product from a row-major tile: column d0 + r, the
+// four rows from k0 and the four from k1.
+template <int P>
+__device__ __forceinline__ u32x4 tr_pair(const uint16_t (*t)[P], int k0, int k1, int d0, int r) {
+    const u32x2 lo = tr_rows4(t, k0, d0, r);
+    const u32x2 hi = tr_rows4(t, k1, d0, r);
     return u32x4{lo.x, lo.y, hi.x, hi.y};
 }
 
-// The same rows for a transposed LDS tile dst[d][row]: a thread holds one
-// 16-byte chunk (8 columns) of a row pair (2p, 2p + 1) and writes each
-// column's pair as one 32-bit word.  Consecutive lanes take consecutive chunks
-// of the same row pair, so every global load instruction reads whole rows.
-template <int D>
-struct PairChunks {
-    static constexpr int kChunks = D / 8;
-    static constexpr int kPer = (kRows / 2) * kChunks / kThreads;   // row-pair chunks per thread
-    u32x4 a[kPer], b[kPer];
-    __device__ __forceinline__ static int pair(int j) { return (threadIdx.x + kThreads * j) / kChunks; }
-    __device__ __forceinline__ static int col(int j) { return ((threadIdx.x + kThreads * j) % kChunks) * 8; }
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t src, int row0) {
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-            a[j] = bload16<D>(src, row0 + 2 * pair(j), col(j));
-            b[j] = bload16<D>(src, row0 + 2 * pair(j) + 1, col(j));
-        }
-    }
-    // The same rows, row-major (no second global load of the tile).
-    __device__ __forceinline__ void store_rows(uint16_t (*dst)[D + kPadRow]) const {
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-            *reinterpret_cast<u32x4*>(&dst[2 * pair(j)][col(j)]) = a[j];
-            *reinterpret_cast<u32x4*>(&dst[2 * pair(j) + 1][col(j)]) = b[j];
-        }
-    }
-    __device__ __forceinline__ void store(uint16_t (*dst)[kPitchT]) const {
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t wa = a[j][e / 2], wb = b[j][e / 2];
-                const uint32_t lo = (e & 1) ? (wa >> 16) : (wa & 0xffffu);
-                const uint32_t hi = (e & 1) ? (wb & 0xffff0000u) : (wb << 16);
-                const int d = col(j) + e;
-                *reinterpret_cast<uint32_t*>(&dst[d][2 * tswz<D>(d, pair(j))]) = lo | hi;
-            }
-        }
-    }
-};
-
-template <int D>
-__device__ __forceinline__ void stage_rows(__amdgpu_buffer_rsrc_t src, int row0, uint16_t (*dst)[D + kPadRow]) {
-    RowChunks<D> t;
-    t.load(src, row0);
-    t.store(dst);
-}
-
-template <int D>
-__device__ __forceinline__ void stage_transposed(__amdgpu_buffer_rsrc_t src, int row0, uint16_t (*dst)[kPitchT]) {
-    PairChunks<D> t;
-    t.load(src, row0);
-    t.store(dst);
-}
-
-// Pipeline over the key tiles of one (batch, head): two register stages, so
-// while tile i is computed from LDS the loads of tiles i + 1 and i + 2 are in
-// flight.  `load(stage, row0)` issues a tile's global loads into a stage,
-// `store(stage)` writes a stage to LDS, `compute(row0)` runs a tile's
-// products from LDS.
-// The loads are unconditional: tiles past the end are outside the buffer
-// resource, so they read zero without touching memory.  Tiles are processed in
-// pairs (an odd last tile is paired with an all-padding tile whose keys the
-// products mask out), so the loop body is straight-line and every path into
-// the loop head has the same loads outstanding: the compiler then waits for
-// just the older stage.
+// Pipeline over a sequence of n_tiles 64-row tiles: two register stages, so
+// while tile t is computed from LDS the loads of tiles t + 1 and t + 2 are in
+// flight.  `load(stage, t)` issues tile t's global loads into a stage,
+// `store(stage)` writes a stage to LDS, `compute(t)` runs tile t's products
+// from LDS.  The loads are unconditional: tiles past the end lie outside the
+// buffer resources, so they read zero without touching memory.  Tiles are
+// processed in pairs (an odd last tile is paired with an all-padding tile
+// whose keys the products mask out), so the loop body is straight-line and
+// every path into the loop head has the same loads outstanding: the compiler
+// then waits for just the older stage.
 template <class Stage, class Load, class Store, class Compute>
-__device__ __forceinline__ void two_stage_tiles(int n_rows, Stage& s0, Stage& s1, Load load, Store store,
+__device__ __forceinline__ void two_stage_tiles(int n_tiles, Stage& s0, Stage& s1, Load load, Store store,
                                                 Compute compute) {
     // The scheduling barriers keep each stage's loads together and in program
     // order (otherwise the two prologue stages interleave and the first
     // stage's wait would cover both).
     load(s0, 0);
     __builtin_amdgcn_sched_barrier(0);
-    load(s1, kRows);
+    load(s1, 1);
     __builtin_amdgcn_sched_barrier(0);
-    for (int row0 = 0; row0 < n_rows; row0 += 2 * kRows) {
+    for (int t = 0; t < n_tiles; t += 2) {
         __syncthreads();
         store(s0);
         __syncthreads();
-        load(s0, row0 + 2 * kRows);
+        load(s0, t + 2);
         __builtin_amdgcn_sched_barrier(0);
-        compute(row0);
+        compute(t);
         __syncthreads();
         store(s1);
         __syncthreads();
-        load(s1, row0 + 3 * kRows);
+        load(s1, t + 3);
         __builtin_amdgcn_sched_barrier(0);
-        compute(row0 + kRows);
+        compute(t + 1);
     }
 }
+
+// The key tiles of one (batch, head): the tiles of the frozen source, then
+// those of the trainable source.  Resources are built once; picking one per
+// tile is a uniform (scalar) choice.
+template <int D>
+struct KeyTiles {
+    __amdgpu_buffer_rsrc_t k[2], v[2];
+    int rows[2];
+    int n0, n;   // tiles of source 0, tiles in total
+    __device__ __forceinline__ KeyTiles(const AttnArgs& a, int b, int h) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const KeySrc& src = a.src[s];
+            const size_t off = ((size_t)(b / src.share) * a.heads + h) * (size_t)src.stride * D;
+            k[s] = mat_rsrc<D>(static_cast<const uint16_t*>(src.k) + off, src.rows);
+            v[s] = mat_rsrc<D>(static_cast<const uint16_t*>(src.v) + off, src.rows);
+            rows[s] = src.rows;
+        }
+        n0 = (rows[0] + kRows - 1) / kRows;
+        n = n0 + (rows[1] + kRows - 1) / kRows;
+    }
+    // Source and first row of tile t (tiles past the end fall past source 1).
+    __device__ __forceinline__ int src_of(int t) const { return t < n0 ? 0 : 1; }
+    __device__ __forceinline__ int row_of(int t) const { return (t < n0 ? t : t - n0) * kRows; }
+    __device__ __forceinline__ int bound_of(int t) const { return t < n0 ? rows[0] : rows[1]; }
+};
 
 // ------------------------------------------------------------------ forward
 
 template <int D>
 struct FwdLds {
-    uint16_t k[kRows][D + kPadRow];   // K tile, row-major
-    uint16_t vt[D][kPitchT];          // V tile, transposed
+    uint16_t k[kRows][D + kPadRow];   // K tile, row-major (read by rows)
+    uint16_t v[kRows][D + kPadTr];    // V tile, row-major (read transposed)
 };
 
 template <int D>
@@ -234,8 +212,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd(AttnArgs a) {
     const int r = lane & 15, g = lane >> 4;
     const size_t bh = (size_t)blockIdx.z * a.heads + blockIdx.y;
     const auto Q = mat_rsrc<D>(static_cast<const uint16_t*>(a.q) + bh * a.lq * D, a.lq);
-    const auto K = mat_rsrc<D>(static_cast<const uint16_t*>(a.k) + bh * a.lk * D, a.lk);
-    const auto V = mat_rsrc<D>(static_cast<const uint16_t*>(a.v) + bh * a.lk * D, a.lk);
+    const KeyTiles<D> kt(a, blockIdx.z, blockIdx.y);
     const int q = blockIdx.x * kRows + 16 * w + r;
     const bool qv = q < a.lq;
     // B operand of S^T = K Q^T: Q[q][32 kk + 8 g .. + 7] (zero past the last query)
@@ -251,7 +228,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd(AttnArgs a) {
     // Products of one staged 64-key tile: the tile's scores, one max and one
     // rescale of the accumulator per tile, then O^T += V^T P^T over two
     // 32-key halves.
-    auto tile = [&](int key0) {
+    auto tile = [&](int t) {
+        const int key0 = kt.row_of(t), bound = kt.bound_of(t);
         f32x4 st[kRows / 16];
 #pragma unroll
         for (int kb = 0; kb < kRows / 16; ++kb) {
@@ -266,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd(AttnArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int key = key0 + 16 * kb + 4 * g + i;
-                st[kb][i] = key < a.lk ? st[kb][i] * sc : -INFINITY;
+                st[kb][i] = key < bound ? st[kb][i] * sc : -INFINITY;
                 bm = fmaxf(bm, st[kb][i]);
             }
         }
@@ -274,7 +252,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd(AttnArgs a) {
         // The first tile always holds key 0, so mn is finite from then on; a
         // padding tile (every key masked) leaves m unchanged and alpha = 1.
         const float mn = fmaxf(m, bm);
-        const float alpha = exp2f(m - mn);
+        const float alpha = exp2_hw(m - mn);
         m = mn;
         float ps = 0.0f;
         u32x2 pb[kRows / 16];
@@ -282,7 +260,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd(AttnArgs a) {
         for (int kb = 0; kb < kRows / 16; ++kb) {
             float p[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) p[i] = exp2f(st[kb][i] - mn);
+            for (int i = 0; i < 4; ++i) p[i] = exp2_hw(st[kb][i] - mn);
             ps += (p[0] + p[1]) + (p[2] + p[3]);
             pb[kb] = u32x2{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
         }
@@ -294,22 +272,22 @@ __global__ __launch_bounds__(kThreads) void attn_fwd(AttnArgs a) {
             const u32x4 bop = {pb[2 * h].x, pb[2 * h].y, pb[2 * h + 1].x, pb[2 * h + 1].y};
 #pragma unroll
             for (int nb = 0; nb < D / 16; ++nb)
-                acc[nb] = mfma32(tpair<D>(s.vt, 16 * nb + r, 32 * h + 4 * g, 32 * h + 16 + 4 * g), bop, acc[nb]);
+                acc[nb] = mfma32(tr_pair(s.v, 32 * h + 4 * g, 32 * h + 16 + 4 * g, 16 * nb, r), bop, acc[nb]);
         }
     };
     struct KV {
-        RowChunks<D> k;
-        PairChunks<D> v;
+        RowChunks<D> k, v;
     } st0, st1;
     two_stage_tiles(
-        a.lk, st0, st1,
-        [&](KV& x, int row0) {
-            x.k.load(K, row0);
-            x.v.load(V, row0);
+        kt.n, st0, st1,
+        [&](KV& x, int t) {
+            const int src = kt.src_of(t), row0 = kt.row_of(t);
+            x.k.load(kt.k[src], row0);
+            x.v.load(kt.v[src], row0);
         },
         [&](const KV& x) {
             x.k.store(s.k);
-            x.v.store(s.vt);
+            x.v.store(s.v);
         },
         tile);
     const float total = group_sum(lsum);
@@ -328,9 +306,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd(AttnArgs a) {
 
 template <int D>
 struct DqLds {
-    uint16_t k[kRows][D + kPadRow];   // K tile, row-major (A of S^T)
-    uint16_t kt[D][kPitchT];          // K tile, transposed (A of dQ^T)
-    uint16_t v[kRows][D + kPadRow];   // V tile, row-major (A of dP^T)
+    uint16_t k[kRows][D + kPadRow];   // K tile, read by rows (A of S^T)
+    uint16_t kr[kRows][D + kPadTr];   // the same K tile, read transposed (A of dQ^T)
+    uint16_t v[kRows][D + kPadRow];   // V tile, read by rows (A of dP^T)
 };
 
 template <int D>
@@ -342,8 +320,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq(AttnArgs a) {
     const auto Q = mat_rsrc<D>(static_cast<const uint16_t*>(a.q) + bh * a.lq * D, a.lq);
     const auto dO = mat_rsrc<D>(static_cast<const uint16_t*>(a.d_o) + bh * a.lq * D, a.lq);
     const auto O = mat_rsrc<D>(static_cast<const uint16_t*>(a.o) + bh * a.lq * D, a.lq);
-    const auto K = mat_rsrc<D>(static_cast<const uint16_t*>(a.k) + bh * a.lk * D, a.lk);
-    const auto V = mat_rsrc<D>(static_cast<const uint16_t*>(a.v) + bh * a.lk * D, a.lk);
+    const KeyTiles<D> kt(a, blockIdx.z, blockIdx.y);
     const int q = blockIdx.x * kRows + 16 * w + r;
     const bool qv = q < a.lq;
     u32x4 qb[D / 32], db[D / 32];
@@ -364,7 +341,8 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq(AttnArgs a) {
 #pragma unroll
     for (int nb = 0; nb < D / 16; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto tile = [&](int key0) {
+    auto tile = [&](int t) {
+        const int key0 = kt.row_of(t), bound = kt.bound_of(t);
         u32x2 dsb[kRows / 16];
 #pragma unroll
         for (int kb = 0; kb < kRows / 16; ++kb) {
@@ -378,7 +356,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq(AttnArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int key = key0 + 16 * kb + 4 * g + i;
-                const float p = key < a.lk ? exp2f(st[i] * sc - lse2) : 0.0f;
+                const float p = key < bound ? exp2_hw(st[i] * sc - lse2) : 0.0f;
                 ds[i] = p * (dpt[i] - delta);
             }
             dsb[kb] = u32x2{pack_bf16(ds[0], ds[1]), pack_bf16(ds[2], ds[3])};
@@ -389,23 +367,23 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq(AttnArgs a) {
             const u32x4 bop = {dsb[2 * h].x, dsb[2 * h].y, dsb[2 * h + 1].x, dsb[2 * h + 1].y};
 #pragma unroll
             for (int nb = 0; nb < D / 16; ++nb)
-                acc[nb] = mfma32(tpair<D>(s.kt, 16 * nb + r, 32 * h + 4 * g, 32 * h + 16 + 4 * g), bop, acc[nb]);
+                acc[nb] = mfma32(tr_pair(s.kr, 32 * h + 4 * g, 32 * h + 16 + 4 * g, 16 * nb, r), bop, acc[nb]);
         }
     };
-    // K is loaded once as row pairs and written both row-major and transposed.
+    // K is loaded once and written twice, at the pitch of each way it is read.
     struct KV {
-        PairChunks<D> k;
-        RowChunks<D> v;
+        RowChunks<D> k, v;
     } st0, st1;
     two_stage_tiles(
-        a.lk, st0, st1,
-        [&](KV& x, int row0) {
-            x.k.load(K, row0);
-            x.v.load(V, row0);
+        kt.n, st0, st1,
+        [&](KV& x, int t) {
+            const int src = kt.src_of(t), row0 = kt.row_of(t);
+            x.k.load(kt.k[src], row0);
+            x.v.load(kt.v[src], row0);
         },
         [&](const KV& x) {
-            x.k.store_rows(s.k);
-            x.k.store(s.kt);
+            x.k.store(s.k);
+            x.k.store(s.kr);
             x.v.store(s.v);
         },
         tile);
@@ -419,10 +397,10 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq(AttnArgs a) {
 
 template <int D>
 struct DkvLds {
-    uint16_t q[kRows][D + kPadRow];    // Q chunk, row-major (A of S)
-    uint16_t d_o[kRows][D + kPadRow];  // dO chunk, row-major (A of dP)
-    uint16_t qt[D][kPitchT];           // Q chunk, transposed (A of dK^T)
-    uint16_t dot[D][kPitchT];          // dO chunk, transposed (A of dV^T)
+    uint16_t q[kRows][D + kPadRow];    // Q chunk, read by rows (A of S)
+    uint16_t d_o[kRows][D + kPadRow];  // dO chunk, read by rows (A of dP)
+    uint16_t qr[kRows][D + kPadTr];    // the same Q chunk, read transposed (A of dK^T)
+    uint16_t dor[kRows][D + kPadTr];   // the same dO chunk, read transposed (A of dV^T)
     float lse2[kRows];
     float delta[kRows];
 };
@@ -433,14 +411,16 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv(AttnArgs a) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
     const size_t bh = (size_t)blockIdx.z * a.heads + blockIdx.y;
-    const int lt = a.lk - a.lk_frozen;
+    const KeySrc& src = a.src[1];
+    const int lt = src.rows;
     const auto Q = mat_rsrc<D>(static_cast<const uint16_t*>(a.q) + bh * a.lq * D, a.lq);
     const auto dO = mat_rsrc<D>(static_cast<const uint16_t*>(a.d_o) + bh * a.lq * D, a.lq);
-    const auto K = mat_rsrc<D>(static_cast<const uint16_t*>(a.k) + bh * a.lk * D, a.lk);
-    const auto V = mat_rsrc<D>(static_cast<const uint16_t*>(a.v) + bh * a.lk * D, a.lk);
+    const size_t koff = ((size_t)(blockIdx.z / src.share) * a.heads + blockIdx.y) * (size_t)src.stride * D;
+    const auto K = mat_rsrc<D>(static_cast<const uint16_t*>(src.k) + koff, lt);
+    const auto V = mat_rsrc<D>(static_cast<const uint16_t*>(src.v) + koff, lt);
     const int j = blockIdx.x * kRows + 16 * w + r;   // trainable key index
     const bool kv = j < lt;
-    const int key = a.lk_frozen + j;
+    const int key = j;
     // B operands: K[key][32 kk + 8 g ..], V[key][32 kk + 8 g ..] (zero past the last key)
     u32x4 kb_[D / 32], vb_[D / 32];
 #pragma unroll
@@ -455,10 +435,15 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv(AttnArgs a) {
 
     for (int q0 = 0; q0 < a.lq; q0 += kRows) {
         __syncthreads();
-        stage_rows<D>(Q, q0, s.q);
-        stage_rows<D>(dO, q0, s.d_o);
-        stage_transposed<D>(Q, q0, s.qt);
-        stage_transposed<D>(dO, q0, s.dot);
+        {
+            RowChunks<D> tq, tdo;
+            tq.load(Q, q0);
+            tdo.load(dO, q0);
+            tq.store(s.q);
+            tq.store(s.qr);
+            tdo.store(s.d_o);
+            tdo.store(s.dor);
+        }
         if (threadIdx.x < kRows) {
             const int qq = q0 + threadIdx.x;
             s.lse2[threadIdx.x] = qq < a.lq ? a.lse[bh * a.lq + qq] * kLog2e : INFINITY;
@@ -479,7 +464,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv(AttnArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int qi = 16 * qb + 4 * g + i;
-                p[i] = exp2f(st[i] * sc - s.lse2[qi]);
+                p[i] = exp2_hw(st[i] * sc - s.lse2[qi]);
                 ds[i] = p[i] * (dpt[i] - s.delta[qi]);
             }
             pb[qb] = u32x2{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
@@ -493,8 +478,8 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv(AttnArgs a) {
 #pragma unroll
             for (int nb = 0; nb < D / 16; ++nb) {
                 const int k0 = 32 * h + 4 * g, k1 = 32 * h + 16 + 4 * g;
-                dv[nb] = mfma32(tpair<D>(s.dot, 16 * nb + r, k0, k1), pop, dv[nb]);
-                dk[nb] = mfma32(tpair<D>(s.qt, 16 * nb + r, k0, k1), dop, dk[nb]);
+                dv[nb] = mfma32(tr_pair(s.dor, k0, k1, 16 * nb, r), pop, dv[nb]);
+                dk[nb] = mfma32(tr_pair(s.qr, k0, k1, 16 * nb, r), dop, dk[nb]);
             }
         }
     }
@@ -521,7 +506,7 @@ hipError_t launch_bwd(const AttnArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(attn_bwd_dq<D>, grid_q, dim3(kThreads), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int lt = a.lk - a.lk_frozen;
+    const int lt = a.src[1].rows;
     if (lt > 0) {
         dim3 grid_k((lt + kRows - 1) / kRows, a.heads, a.batch);
         hipLaunchKernelGGL(attn_bwd_dkdv<D>, grid_k, dim3(kThreads), 0, st, a);

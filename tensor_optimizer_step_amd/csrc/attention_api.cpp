@@ -19,14 +19,38 @@ using namespace somaopt;
 
 namespace {
 
+// Rows per matrix are bounded so that every byte offset of a buffer
+// resource (including the padding tiles past the end) fits in 31 bits.
+constexpr int32_t kMaxRows = 1 << 22;
+
+int check_common(int32_t batch, int32_t heads, int32_t lq, int32_t head_dim, float scale) {
+    if (head_dim != 64 && head_dim != 128) return set_error(SOMAOPT_E_INVALID, "head_dim must be 64 or 128");
+    if (batch < 1 || heads < 1 || batch > 65535 || heads > 65535)
+        return set_error(SOMAOPT_E_INVALID, "batch and heads must be in [1, 65535]");
+    if (lq < 1 || lq > kMaxRows) return set_error(SOMAOPT_E_INVALID, "lq must be in [1, 2^22]");
+    if (!(scale == scale) || scale == 0.0f || scale - scale != 0.0f)
+        return set_error(SOMAOPT_E_INVALID, "scale must be finite and nonzero");
+    return SOMAOPT_OK;
+}
+
 int check_shape(const somaopt_attn_shape* s) {
     if (!s) return set_error(SOMAOPT_E_INVALID, "shape is NULL");
-    if (s->head_dim != 64 && s->head_dim != 128) return set_error(SOMAOPT_E_INVALID, "head_dim must be 64 or 128");
-    if (s->batch < 1 || s->heads < 1 || s->batch > 65535 || s->heads > 65535)
-        return set_error(SOMAOPT_E_INVALID, "batch and heads must be in [1, 65535]");
-    if (s->lq < 1 || s->lk < 1) return set_error(SOMAOPT_E_INVALID, "lq and lk must be >= 1");
+    int rc = check_common(s->batch, s->heads, s->lq, s->head_dim, s->scale);
+    if (rc) return rc;
+    if (s->lk < 1 || s->lk > kMaxRows) return set_error(SOMAOPT_E_INVALID, "lk must be in [1, 2^22]");
     if (s->lk_frozen < 0 || s->lk_frozen > s->lk) return set_error(SOMAOPT_E_INVALID, "lk_frozen outside [0, lk]");
-    if (!(s->scale == s->scale) || s->scale == 0.0f) return set_error(SOMAOPT_E_INVALID, "scale must be finite and nonzero");
+    return SOMAOPT_OK;
+}
+
+int check_ctx_shape(const somaopt_attn_ctx_shape* s) {
+    if (!s) return set_error(SOMAOPT_E_INVALID, "shape is NULL");
+    int rc = check_common(s->batch, s->heads, s->lq, s->head_dim, s->scale);
+    if (rc) return rc;
+    if (s->l_ctx < 0 || s->l_ctx > kMaxRows || s->l_act < 0 || s->l_act > kMaxRows)
+        return set_error(SOMAOPT_E_INVALID, "l_ctx and l_act must be in [0, 2^22]");
+    if (s->l_ctx + s->l_act < 1) return set_error(SOMAOPT_E_INVALID, "l_ctx + l_act must be >= 1");
+    if (s->ctx_share < 1 || s->batch % s->ctx_share != 0)
+        return set_error(SOMAOPT_E_INVALID, "ctx_share must be >= 1 and divide batch");
     return SOMAOPT_OK;
 }
 
@@ -58,17 +82,40 @@ int check_buffer(const void* p, size_t bytes, size_t align, const char* name) {
     return SOMAOPT_OK;
 }
 
-AttnArgs make_args(const somaopt_attn_shape* s) {
+AttnArgs base_args(int32_t batch, int32_t heads, int32_t lq, int32_t head_dim, float scale) {
     AttnArgs a;
     std::memset(&a, 0, sizeof(a));
-    a.batch = s->batch;
-    a.heads = s->heads;
-    a.lq = s->lq;
-    a.lk = s->lk;
-    a.lk_frozen = s->lk_frozen;
-    a.head_dim = s->head_dim;
-    a.scale = s->scale;
+    a.batch = batch;
+    a.heads = heads;
+    a.lq = lq;
+    a.head_dim = head_dim;
+    a.scale = scale;
     return a;
+}
+
+// One buffer of lk keys per (batch, head): rows [0, lk_frozen) are source 0,
+// rows [lk_frozen, lk) source 1, both with stride lk.
+AttnArgs make_args(const somaopt_attn_shape* s, const void* k, const void* v) {
+    AttnArgs a = base_args(s->batch, s->heads, s->lq, s->head_dim, s->scale);
+    const size_t skip = (size_t)s->lk_frozen * s->head_dim * 2;
+    a.src[0] = KeySrc{k, v, s->lk_frozen, s->lk, 1};
+    a.src[1] = KeySrc{static_cast<const char*>(k) + skip, static_cast<const char*>(v) + skip, s->lk - s->lk_frozen,
+                      s->lk, 1};
+    return a;
+}
+
+// Separate context (shared by ctx_share consecutive query batches) and
+// action buffers.  An empty source keeps a valid (unused) pointer.
+AttnArgs make_ctx_args(const somaopt_attn_ctx_shape* s, const void* kc, const void* vc, const void* ka,
+                       const void* va) {
+    AttnArgs a = base_args(s->batch, s->heads, s->lq, s->head_dim, s->scale);
+    a.src[0] = KeySrc{s->l_ctx ? kc : ka, s->l_ctx ? vc : va, s->l_ctx, s->l_ctx, s->ctx_share};
+    a.src[1] = KeySrc{s->l_act ? ka : kc, s->l_act ? va : vc, s->l_act, s->l_act, 1};
+    return a;
+}
+
+int launch_rc(hipError_t e, const char* what) {
+    return e == hipSuccess ? SOMAOPT_OK : set_error(SOMAOPT_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
 }  // namespace
@@ -85,15 +132,11 @@ int somaopt_attn_forward(const void* q, const void* k, const void* v, void* o, f
         (rc = check_buffer(v, nk, 16, "v")) || (rc = check_buffer(o, nq, 16, "o")) ||
         (rc = check_buffer(lse, bh * shape->lq * 4, 4, "lse")))
         return rc;
-    AttnArgs a = make_args(shape);
+    AttnArgs a = make_args(shape, k, v);
     a.q = q;
-    a.k = k;
-    a.v = v;
     a.o = o;
     a.lse = lse;
-    hipError_t e = launch_attention_forward(a, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? SOMAOPT_OK
-                           : set_error(SOMAOPT_E_HIP, std::string("attention forward launch: ") + hipGetErrorString(e));
+    return launch_rc(launch_attention_forward(a, static_cast<hipStream_t>(stream)), "attention forward launch");
 }
 
 int somaopt_attn_backward(const void* q, const void* k, const void* v, const void* o,
@@ -112,10 +155,8 @@ int somaopt_attn_backward(const void* q, const void* k, const void* v, const voi
         return rc;
     if (lt > 0 && ((rc = check_buffer(dk, bh * lt * D * 4, 16, "dk")) || (rc = check_buffer(dv, bh * lt * D * 4, 16, "dv"))))
         return rc;
-    AttnArgs a = make_args(shape);
+    AttnArgs a = make_args(shape, k, v);
     a.q = q;
-    a.k = k;
-    a.v = v;
     a.o = const_cast<void*>(o);
     a.lse = const_cast<float*>(lse);
     a.d_o = d_o;
@@ -123,9 +164,61 @@ int somaopt_attn_backward(const void* q, const void* k, const void* v, const voi
     a.dk = dk;
     a.dv = dv;
     a.delta = delta;
-    hipError_t e = launch_attention_backward(a, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? SOMAOPT_OK
-                           : set_error(SOMAOPT_E_HIP, std::string("attention backward launch: ") + hipGetErrorString(e));
+    return launch_rc(launch_attention_backward(a, static_cast<hipStream_t>(stream)), "attention backward launch");
+}
+
+int somaopt_attn_ctx_forward(const void* q, const void* k_ctx, const void* v_ctx, const void* k_act,
+                             const void* v_act, void* o, float* lse, const somaopt_attn_ctx_shape* shape,
+                             void* stream) {
+    int rc = check_ctx_shape(shape);
+    if (rc) return rc;
+    const size_t bh = (size_t)shape->batch * shape->heads, D = (size_t)shape->head_dim;
+    const size_t nq = bh * shape->lq * D * 2;
+    const size_t nc = bh / shape->ctx_share * shape->l_ctx * D * 2, na = bh * shape->l_act * D * 2;
+    if ((rc = check_buffer(q, nq, 16, "q")) || (rc = check_buffer(o, nq, 16, "o")) ||
+        (rc = check_buffer(lse, bh * shape->lq * 4, 4, "lse")))
+        return rc;
+    if (shape->l_ctx && ((rc = check_buffer(k_ctx, nc, 16, "k_ctx")) || (rc = check_buffer(v_ctx, nc, 16, "v_ctx"))))
+        return rc;
+    if (shape->l_act && ((rc = check_buffer(k_act, na, 16, "k_act")) || (rc = check_buffer(v_act, na, 16, "v_act"))))
+        return rc;
+    AttnArgs a = make_ctx_args(shape, k_ctx, v_ctx, k_act, v_act);
+    a.q = q;
+    a.o = o;
+    a.lse = lse;
+    return launch_rc(launch_attention_forward(a, static_cast<hipStream_t>(stream)), "attention forward launch");
+}
+
+int somaopt_attn_ctx_backward(const void* q, const void* k_ctx, const void* v_ctx, const void* k_act,
+                              const void* v_act, const void* o, const float* lse, const void* d_o, float* dq,
+                              float* dk_act, float* dv_act, float* delta, const somaopt_attn_ctx_shape* shape,
+                              void* stream) {
+    int rc = check_ctx_shape(shape);
+    if (rc) return rc;
+    const size_t bh = (size_t)shape->batch * shape->heads, D = (size_t)shape->head_dim;
+    const size_t nq = bh * shape->lq * D * 2;
+    const size_t nc = bh / shape->ctx_share * shape->l_ctx * D * 2, na = bh * shape->l_act * D * 2;
+    if ((rc = check_buffer(q, nq, 16, "q")) || (rc = check_buffer(o, nq, 16, "o")) ||
+        (rc = check_buffer(d_o, nq, 16, "d_o")) || (rc = check_buffer(lse, bh * shape->lq * 4, 4, "lse")) ||
+        (rc = check_buffer(delta, bh * shape->lq * 4, 4, "delta")) ||
+        (rc = check_buffer(dq, bh * shape->lq * D * 4, 16, "dq")))
+        return rc;
+    if (shape->l_ctx && ((rc = check_buffer(k_ctx, nc, 16, "k_ctx")) || (rc = check_buffer(v_ctx, nc, 16, "v_ctx"))))
+        return rc;
+    if (shape->l_act && ((rc = check_buffer(k_act, na, 16, "k_act")) || (rc = check_buffer(v_act, na, 16, "v_act")) ||
+                         (rc = check_buffer(dk_act, na * 2, 16, "dk_act")) ||
+                         (rc = check_buffer(dv_act, na * 2, 16, "dv_act"))))
+        return rc;
+    AttnArgs a = make_ctx_args(shape, k_ctx, v_ctx, k_act, v_act);
+    a.q = q;
+    a.o = const_cast<void*>(o);
+    a.lse = const_cast<float*>(lse);
+    a.d_o = d_o;
+    a.dq = dq;
+    a.dk = dk_act;
+    a.dv = dv_act;
+    a.delta = delta;
+    return launch_rc(launch_attention_backward(a, static_cast<hipStream_t>(stream)), "attention backward launch");
 }
 
 }  // extern "C"

@@ -68,6 +68,12 @@ class AttnShape(ctypes.Structure):
                 ("scale", ctypes.c_float)]
 
 
+class AttnCtxShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("lq", ctypes.c_int32),
+                ("l_ctx", ctypes.c_int32), ("l_act", ctypes.c_int32), ("ctx_share", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
 _P = ctypes.c_void_p
 _PP = ctypes.POINTER(ctypes.c_void_p)
 # name -> (restype, argtypes); mirrors include/somaopt.h
@@ -94,6 +100,10 @@ SIGNATURES = {
     "somaopt_attn_forward": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.POINTER(AttnShape), _P]),
     "somaopt_attn_backward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                              ctypes.POINTER(AttnShape), _P]),
+    "somaopt_attn_ctx_forward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, ctypes.POINTER(AttnCtxShape),
+                                                _P]),
+    "somaopt_attn_ctx_backward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                                 ctypes.POINTER(AttnCtxShape), _P]),
     "somaopt_destroy": (None, [_P]),
     "somaopt_last_error": (ctypes.c_char_p, []),
     "somaopt_version": (ctypes.c_char_p, []),
@@ -334,6 +344,34 @@ def attn_backward(q, k, v, o, lse, d_o, dq, dk, dv, delta, lk_frozen: int,
     _check(load().somaopt_attn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(d_o),
                                         _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta), ctypes.byref(sh),
                                         _stream_ptr(stream)))
+
+
+def attn_ctx_shape(q, k_ctx, k_act, ctx_share: int = 1, scale: Optional[float] = None) -> AttnCtxShape:
+    """Shape of bf16 q [B, H, Lq, D], k_ctx [B / ctx_share, H, Lc, D] (or None)
+    and k_act [B, H, La, D] (or None)."""
+    b, h, lq, d = q.shape
+    lc = 0 if k_ctx is None else k_ctx.shape[2]
+    la = 0 if k_act is None else k_act.shape[2]
+    return AttnCtxShape(b, h, lq, lc, la, int(ctx_share), d, float(scale if scale is not None else d ** -0.5))
+
+
+def attn_ctx_forward(q, k_ctx, v_ctx, k_act, v_act, o, lse, ctx_share: int = 1,
+                     scale: Optional[float] = None, stream=None):
+    """Attention over a frozen context (shared by ``ctx_share`` consecutive query
+    batches) followed by trainable action keys; either may be None."""
+    sh = attn_ctx_shape(q, k_ctx, k_act, ctx_share, scale)
+    _check(load().somaopt_attn_ctx_forward(_ptr(q), _ptr(k_ctx), _ptr(v_ctx), _ptr(k_act), _ptr(v_act),
+                                           _ptr(o), _ptr(lse), ctypes.byref(sh), _stream_ptr(stream)))
+
+
+def attn_ctx_backward(q, k_ctx, v_ctx, k_act, v_act, o, lse, d_o, dq, dk_act, dv_act, delta,
+                      ctx_share: int = 1, scale: Optional[float] = None, stream=None):
+    """dQ for every query; dK, dV (fp32, shaped like k_act) for the action keys."""
+    sh = attn_ctx_shape(q, k_ctx, k_act, ctx_share, scale)
+    _check(load().somaopt_attn_ctx_backward(_ptr(q), _ptr(k_ctx), _ptr(v_ctx), _ptr(k_act), _ptr(v_act),
+                                            _ptr(o), _ptr(lse), _ptr(d_o), _ptr(dq), _ptr(dk_act),
+                                            _ptr(dv_act), _ptr(delta), ctypes.byref(sh),
+                                            _stream_ptr(stream)))
 
 
 def version() -> str:

@@ -118,3 +118,81 @@ def test_attention_rejects_bad_shapes():
     with pytest.raises(somaopt.SomaoptError, match="aligned"):
         somaopt._check(lib.somaopt_attn_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                                 lse.data_ptr() + 2, somaopt.ctypes.byref(sh), None))
+
+
+# Separate frozen-context and trainable-action buffers (landing page, paragraph
+# 6): a context shared by consecutive query batches (flow timesteps), cross-
+# attention to frozen features only, trainable keys only, ragged tiles.
+CTX_CASES = [
+    # b, h, lq, l_ctx, l_act, ctx_share, d
+    (6, 2, 50, 300, 40, 3, 128),
+    (2, 3, 64, 128, 0, 1, 64),
+    (2, 2, 33, 0, 70, 1, 128),
+    (4, 1, 17, 65, 1, 2, 64),
+    (2, 2, 130, 7, 129, 1, 128),
+]
+
+
+@pytest.mark.parametrize("case", CTX_CASES, ids=lambda c: "b{}h{}q{}c{}a{}s{}d{}".format(*c))
+def test_attention_context_and_action_buffers(case):
+    from tensor_optimizer_step_amd import somaopt
+    b, h, lq, lc, la, share, d = case
+    log(f"[attention ctx] case {case}")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1000 + sum(case))
+    mk = lambda *s: torch.randn(*s, generator=g, device="cuda").to(torch.bfloat16)
+    q, do = mk(b, h, lq, d), mk(b, h, lq, d)
+    kc = mk(b // share, h, lc, d) if lc else None
+    vc = mk(b // share, h, lc, d) if lc else None
+    ka = mk(b, h, la, d) if la else None
+    va = mk(b, h, la, d) if la else None
+    scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q)
+    lse = torch.empty(b, h, lq, device="cuda")
+    somaopt.attn_ctx_forward(q, kc, vc, ka, va, o, lse, share, scale)
+    dq = torch.empty(b, h, lq, d, device="cuda")
+    dk = torch.empty(b, h, la, d, device="cuda") if la else None
+    dv = torch.empty(b, h, la, d, device="cuda") if la else None
+    delta = torch.empty(b, h, lq, device="cuda")
+    somaopt.attn_ctx_backward(q, kc, vc, ka, va, o, lse, do, dq, dk, dv, delta, share, scale)
+    torch.cuda.synchronize()
+    # the oracle sees, per query batch, the context of batch // share followed
+    # by that batch's action keys
+    parts_k, parts_v = [], []
+    if lc:
+        parts_k.append(np.repeat(_host(kc), share, axis=0))
+        parts_v.append(np.repeat(_host(vc), share, axis=0))
+    if la:
+        parts_k.append(_host(ka))
+        parts_v.append(_host(va))
+    hk, hv = np.concatenate(parts_k, axis=2), np.concatenate(parts_v, axis=2)
+    hq, hdo, ho, hlse = _host(q), _host(do), _host(o), lse.cpu().numpy()
+    o_ref, lse_ref = O.attention_forward(hq, hk, hv, scale)
+    bud = O.error_budget_forward(hq, hk, hv, lse_ref, scale) + 2.0 ** -8 * np.abs(o_ref)
+    wo = _within("O", O.attention_fp64._f64(ho), o_ref, bud)
+    wl = _within("LSE", hlse, lse_ref, 1e-5 * (1.0 + np.abs(lse_ref)))
+    dq_ref, dk_ref, dv_ref = O.attention_backward(hq, hk, hv, ho, hlse, hdo, scale, lc)
+    bq, bk, bv = O.error_budget_backward(hq, hk, hv, ho, hlse, hdo, scale, lc)
+    wq = _within("dQ", dq.cpu().numpy(), dq_ref, bq)
+    wk = wv = 0.0
+    if la:
+        wk = _within("dK", dk.cpu().numpy(), dk_ref, bk)
+        wv = _within("dV", dv.cpu().numpy(), dv_ref, bv)
+    log(f"[attention ctx] {case}: worst error / budget O {wo:.3f} LSE {wl:.3f} dQ {wq:.3f} dK {wk:.3f} dV {wv:.3f}")
+
+
+def test_attention_context_rejects_bad_shapes():
+    from tensor_optimizer_step_amd import somaopt
+    q = torch.zeros(3, 1, 8, 64, device="cuda", dtype=torch.bfloat16)
+    kc = torch.zeros(1, 1, 8, 64, device="cuda", dtype=torch.bfloat16)
+    o = torch.empty_like(q)
+    lse = torch.empty(3, 1, 8, device="cuda")
+    with pytest.raises(somaopt.SomaoptError, match="ctx_share"):
+        somaopt.attn_ctx_forward(q, kc, kc, None, None, o, lse, ctx_share=2)
+    with pytest.raises(somaopt.SomaoptError, match="l_ctx \\+ l_act"):
+        somaopt.attn_ctx_forward(q, None, None, None, None, o, lse)
+    lib = somaopt.load()
+    sh = somaopt.AttnCtxShape(3, 1, 8, 8, 0, 1, 64, 0.125)
+    with pytest.raises(somaopt.SomaoptError, match="k_ctx is NULL"):
+        somaopt._check(lib.somaopt_attn_ctx_forward(q.data_ptr(), None, kc.data_ptr(), None, None, o.data_ptr(),
+                                                    lse.data_ptr(), somaopt.ctypes.byref(sh), None))
