@@ -8,3 +8,4 @@ from .adamw_fp64 import (CLIP_EPS, Group, Oracle, StepStats, adamw_update,  # no
                          round_to_bf16_bits, round_to_f16, update_elements, widen_grad)
 from .attention_fp64 import (attention_backward, attention_forward, attention_probs,  # noqa: F401
                              error_budget_backward, error_budget_forward)
+from .accumulate_fp64 import accumulate_gradient  # noqa: F401

@@ -87,9 +87,10 @@ def round_to_f16(x: np.ndarray) -> np.ndarray:
 def normalized_sumsq(grads: Sequence[np.ndarray], owned: Sequence[bool], divisor: float) -> float:
     """Sum over owned tensors of the squared effective-batch-normalized gradient.
 
-    Landing page: "normalize those gradients for the effective batch, measure
-    their overall magnitude"; ownership: each shard contributes once.
-    Tensors are summed in list order.
+    Landing page, paragraph 7: the gradients are normalized for the effective
+    batch before their overall magnitude is measured; paragraph 8: under
+    distributed ownership every shard enters once.  Tensors are summed in list
+    order.
     """
     total = 0.0
     for g, own in zip(grads, owned):
