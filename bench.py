@@ -44,6 +44,9 @@ def parse():
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     ap.add_argument("--lowp", choices=["none", "bf16", "f16"], default="none",
                     help="also write a low-precision working copy of the weights (+2 B/element)")
+    ap.add_argument("--arrival", choices=["none", "copy", "accumulate"], default="none",
+                    help="time the step as the gradient-arrival pass (copy or accumulate the arriving "
+                         "gradients, norm fused in) followed by the update pass")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for HBM counter scaling)")
     return ap.parse_args()
@@ -308,6 +311,61 @@ def attention_bench(torch, args):
     print(json.dumps(out), flush=True)
 
 
+def arrival_bench(torch, args, wl, opt, keep, stream, bts):
+    """The step with the gradient-arrival pass: K x {arrival + norm, update},
+    eager launches, against K x {arrival, separate norm pass, update} on the
+    same buffers (the order the passes would take unfused)."""
+    from tensor_optimizer_step_amd import workloads as W
+    grads = keep[1]
+    inc = [torch.empty_like(g) for g in grads]
+    for i, x in enumerate(inc):
+        x.copy_(W.grad_values(wl, i, 2, "cuda"))
+    opt.register_arrival(inc, stream)
+    acc = args.arrival == "accumulate"
+    gsz = sum((4 if t.grad_dtype == W.F32 else 2) * t.numel for t in wl.tensors if t.trainable)
+    arrival_bytes = gsz * (3 if acc else 2)
+
+    def run(separate_norm, reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(args.warmup):
+            opt.arrival_sqnorm(acc, stream)
+            opt.fused_adamw_step(stream)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            opt.arrival_sqnorm(acc, stream)
+            if separate_norm:
+                opt.grad_sqnorm(stream)
+            opt.fused_adamw_step(stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms_fused = run(False, args.steps)
+    ms_sep = run(True, args.steps)
+    stats, _ = opt.read_stats()
+    if not all(math.isfinite(x) for x in (stats.norm, stats.clip_coef)):
+        raise RuntimeError("non-finite statistics in the benchmark run")
+    n_elem = wl.trainable_numel
+    fused_bytes = arrival_bytes + bts["pass2"]
+    sep_bytes = arrival_bytes + bts["pass1"] + bts["pass2"]
+    out = {
+        "metric": "gradient arrival with fused norm + AdamW update: param-elements/s and achieved HBM GB/s",
+        "value": n_elem / (ms_fused * 1e-3), "unit": "param-elements/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_fused, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "hbm_GBps": round(fused_bytes / ms_fused / 1e6, 1),
+        "hbm_frac_of_peak": round(fused_bytes / ms_fused / 1e6 / HBM_PEAK_GBS, 4),
+        "config": {"workload": wl.name, "arrival": args.arrival, "trainable_elements": n_elem,
+                   "model_bytes_per_step": fused_bytes},
+        "separate_norm_pass": {"ms_per_step": ms_sep, "model_bytes_per_step": sep_bytes,
+                               "hbm_GBps": round(sep_bytes / ms_sep / 1e6, 1)},
+        "saved_ms_per_step": ms_sep - ms_fused,
+    }
+    opt.close()
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -345,6 +403,12 @@ def main():
         bts["pass1"] = 2 * info_owned
         bts["total"] = bts["pass1"] + bts["pass2"]
     n_elem = wl.trainable_numel
+
+    if args.arrival != "none":
+        if args.workload == "sharded_7b":
+            raise SystemExit("--arrival is measured on the unsharded workloads")
+        arrival_bench(torch, args, wl, opt, keep, stream, bts)
+        return
 
     # warm-up, then exactly K timed replays of the captured step
     for k in range(args.warmup):

@@ -198,6 +198,40 @@ int somaopt_grad_sqnorm(somaopt_handle* h, void* stream);
  */
 int somaopt_fused_adamw_step(somaopt_handle* h, void* stream);
 
+/*
+ * Gradient arrival with the norm pass fused in -- the step just before the
+ * optimizer path.  With sharded state (landing page, paragraph 1) every GPU
+ * receives its already-reduced gradient shard after backward and adds it into
+ * the gradient shard it holds; the fused optimizer then first needs the owned
+ * sum of squares of those gradients (paragraph 8).  Doing both in one pass
+ * removes the norm pass's separate read of every gradient.
+ *
+ * somaopt_register_arrival, once per handle: incoming[i] is the device buffer
+ * whose values arrive for descriptor i (same numel, gradient dtype and element
+ * order as its grad; ignored and may be NULL for frozen descriptors).  The
+ * buffers must stay at these addresses for the handle's lifetime.  The arrival
+ * pass writes the gradients, so for registration gradients must not overlap
+ * one another or any param/exp_avg/exp_avg_sq/working copy, and no incoming
+ * buffer may overlap any of those or any gradient (incoming buffers may
+ * overlap each other).  Builds a device table (synchronizes `stream` once).
+ * SOMAOPT_E_INVALID on a bad pointer, overlap or count; SOMAOPT_E_STATE if
+ * already registered.
+ *
+ * somaopt_arrival_sqnorm: for every trainable descriptor
+ *     accumulate = 0:  grad <- incoming                      (bitwise copy)
+ *     accumulate = 1:  grad <- round(grad + incoming)        (fp32 sum of the
+ *                      exactly widened values, rounded once to the gradient
+ *                      dtype, nearest even; fp32 gradients: the fp32 sum)
+ * then, on the new gradients, exactly the statistics somaopt_grad_sqnorm
+ * would produce (owned fp64 sum of squares in a fixed order, norm, clip
+ * coefficient, per-group constants; the step count advances once per pending
+ * update).  It takes the place of somaopt_grad_sqnorm: the next
+ * somaopt_fused_adamw_step applies the update.  SOMAOPT_E_STATE before
+ * registration.
+ */
+int somaopt_register_arrival(somaopt_handle* h, const void* const* incoming, int64_t n_tensors, void* stream);
+int somaopt_arrival_sqnorm(somaopt_handle* h, int32_t accumulate, void* stream);
+
 /* Replace every group's hyperparameters (n_groups must equal the handle's).
  * Enqueued as a tiny kernel whose arguments carry the values, so the host
  * array may be reused at once; a learning-rate schedule calls this before

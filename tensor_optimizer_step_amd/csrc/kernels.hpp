@@ -57,6 +57,22 @@ struct Pass1Args {
     uint32_t lds_bytes;          // LDS reserved per workgroup (occupancy limit)
 };
 
+// Arrival pass: rewrites every trainable gradient from its arriving buffer
+// and writes one owned sum-of-squares partial per workgroup; the reduction and
+// finalize of the norm pass then run on those partials.
+struct Pass3Args {
+    const Seg3* segs;
+    const uint32_t* blk_first;   // n_blocks + 1 entries
+    uint32_t n_blocks;           // >= 1
+    double* partials;            // n_blocks entries
+    double* partials2;           // ceil(n_blocks / kReduceSpan) entries (two-level only)
+    DevState* state;
+    int32_t n_groups;
+    int32_t advance;             // 1: this pass opens a new update (t += 1)
+    int32_t accumulate;          // 1: g = round(g + incoming); 0: g = incoming
+    uint32_t lds_bytes;          // LDS reserved per workgroup (occupancy limit)
+};
+
 struct Pass2Args {
     const Seg2* segs;
     const uint32_t* blk_first;
@@ -67,6 +83,7 @@ struct Pass2Args {
 
 hipError_t launch_pass1(const Pass1Args& a, hipStream_t s);
 hipError_t launch_pass2(const Pass2Args& a, hipStream_t s);
+hipError_t launch_pass3(const Pass3Args& a, hipStream_t s);
 hipError_t launch_set_groups(DevState* st, const GroupArgs& g, hipStream_t s);
 hipError_t launch_set_clip(DevState* st, double max_norm, double grad_divisor, hipStream_t s);
 hipError_t launch_set_step(DevState* st, int64_t step, int32_t n_groups, hipStream_t s);

@@ -12,10 +12,42 @@ namespace {
 struct Interval {
     uintptr_t lo, hi;   // [lo, hi)
     int64_t tensor;
-    int kind;           // 0 p, 1 m, 2 v, 3 g, 4 working copy
+    int kind;           // 0 p, 1 m, 2 v, 3 g, 4 working copy, 5 arriving gradient
 };
 
-const char* kKindName[5] = {"param", "exp_avg", "exp_avg_sq", "grad", "param_lowp"};
+const char* kKindName[6] = {"param", "exp_avg", "exp_avg_sq", "grad", "param_lowp", "incoming"};
+
+// Sorted sweep over [lo, hi) intervals: a writable interval may overlap
+// nothing; a read-only one may overlap other read-only ones only.
+int check_overlaps(std::vector<Interval>& iv, int readonly_kind, std::string& err) {
+    std::sort(iv.begin(), iv.end(), [](const Interval& x, const Interval& y) {
+        return x.lo < y.lo || (x.lo == y.lo && x.hi < y.hi);
+    });
+    // Keep the interval with the furthest end among writable ones and among
+    // read-only ones separately.
+    uintptr_t w_end = 0, r_end = 0;
+    int64_t w_t = -1, r_t = -1;
+    int w_k = 0, r_k = 0;
+    for (const Interval& x : iv) {
+        const bool writable = x.kind != readonly_kind;
+        if (w_t >= 0 && x.lo < w_end) {
+            err = std::string("buffers overlap: tensor ") + std::to_string(x.tensor) + " " + kKindName[x.kind] +
+                  " and tensor " + std::to_string(w_t) + " " + kKindName[w_k];
+            return SOMAOPT_E_INVALID;
+        }
+        if (writable && r_t >= 0 && x.lo < r_end) {
+            err = std::string("buffers overlap: tensor ") + std::to_string(x.tensor) + " " + kKindName[x.kind] +
+                  " and tensor " + std::to_string(r_t) + " " + kKindName[r_k];
+            return SOMAOPT_E_INVALID;
+        }
+        if (writable) {
+            if (x.hi > w_end || w_t < 0) { w_end = x.hi; w_t = x.tensor; w_k = x.kind; }
+        } else {
+            if (x.hi > r_end || r_t < 0) { r_end = x.hi; r_t = x.tensor; r_k = x.kind; }
+        }
+    }
+    return SOMAOPT_OK;
+}
 
 std::string fmt(const char* f, long long a = 0, long long b = 0, long long c = 0) {
     char buf[256];
@@ -101,34 +133,41 @@ int validate_host(const somaopt_tensor_desc* d, int64_t n, int32_t n_groups, std
     // Overlap check: written buffers (p, m, v, working copy) may overlap
     // nothing; gradients may overlap other gradients (both read only) but no
     // written buffer.
-    std::sort(iv.begin(), iv.end(), [](const Interval& x, const Interval& y) {
-        return x.lo < y.lo || (x.lo == y.lo && x.hi < y.hi);
-    });
-    // Sweep keeping the interval with the furthest end among writable ones and
-    // among gradients separately.
-    uintptr_t w_end = 0, g_end = 0;
-    int64_t w_t = -1, g_t = -1;
-    int w_k = 0, g_k = 0;
-    for (const Interval& x : iv) {
-        bool writable = x.kind != 3;
-        if (w_t >= 0 && x.lo < w_end) {
-            err = std::string("buffers overlap: tensor ") + std::to_string(x.tensor) + " " +
-                  kKindName[x.kind] + " and tensor " + std::to_string(w_t) + " " + kKindName[w_k];
-            return SOMAOPT_E_INVALID;
-        }
-        if (writable && g_t >= 0 && x.lo < g_end) {
-            err = std::string("buffers overlap: tensor ") + std::to_string(x.tensor) + " " +
-                  kKindName[x.kind] + " and tensor " + std::to_string(g_t) + " " + kKindName[g_k];
-            return SOMAOPT_E_INVALID;
-        }
-        if (writable) {
-            if (x.hi > w_end || w_t < 0) { w_end = x.hi; w_t = x.tensor; w_k = x.kind; }
-        } else {
-            if (x.hi > g_end || g_t < 0) { g_end = x.hi; g_t = x.tensor; g_k = x.kind; }
-        }
-    }
+    if (check_overlaps(iv, 3, err) != SOMAOPT_OK) return SOMAOPT_E_INVALID;
     if (counts) *counts = c;
     return SOMAOPT_OK;
+}
+
+int validate_arrival(const somaopt_tensor_desc* d, int64_t n, const void* const* incoming, std::string& err) {
+    if (n > 0 && incoming == nullptr) { err = "incoming is NULL"; return SOMAOPT_E_INVALID; }
+    std::vector<Interval> iv;
+    for (int64_t i = 0; i < n; ++i) {
+        const somaopt_tensor_desc& t = d[i];
+        if (!t.trainable || t.numel == 0) continue;
+        const void* ptrs[6] = {t.param, t.exp_avg, t.exp_avg_sq, t.grad, t.param_lowp, incoming[i]};
+        const int64_t gsz = grad_elem_bytes(t.grad_dtype);
+        const int64_t esz[6] = {4, 4, 4, gsz, 2, gsz};
+        for (int k = 0; k < 6; ++k) {
+            if (k == 4 && !t.param_lowp) continue;
+            const uintptr_t a = reinterpret_cast<uintptr_t>(ptrs[k]);
+            if (a == 0) {
+                err = std::string("tensor ") + std::to_string(i) + ": " + kKindName[k] + " pointer is NULL";
+                return SOMAOPT_E_INVALID;
+            }
+            if (a % (uintptr_t)esz[k]) {
+                err = std::string("tensor ") + std::to_string(i) + ": " + kKindName[k] +
+                      " pointer is not aligned to its element size";
+                return SOMAOPT_E_INVALID;
+            }
+            const uintptr_t bytes = (uintptr_t)t.numel * (uintptr_t)esz[k];
+            if (a + bytes < a) {
+                err = std::string("tensor ") + std::to_string(i) + ": " + kKindName[k] + " range wraps";
+                return SOMAOPT_E_INVALID;
+            }
+            iv.push_back(Interval{a, a + bytes, i, k});
+        }
+    }
+    return check_overlaps(iv, 5, err);
 }
 
 namespace {
@@ -149,7 +188,8 @@ int64_t common_head(const uintptr_t* addr, const int64_t* esz, int n, int64_t ve
 
 }  // namespace
 
-Plan build_plan(const somaopt_tensor_desc* d, int64_t n, int pass, int64_t chunk, int64_t segment_cost) {
+Plan build_plan(const somaopt_tensor_desc* d, int64_t n, int pass, int64_t chunk, int64_t segment_cost,
+                const void* const* incoming) {
     Plan plan;
     plan.chunk = chunk;
     for (int64_t i = 0; i < n; ++i) {
@@ -163,6 +203,11 @@ Plan build_plan(const somaopt_tensor_desc* d, int64_t n, int pass, int64_t chunk
             uintptr_t a[1] = {reinterpret_cast<uintptr_t>(t.grad)};
             int64_t s[1] = {gsz};
             head = common_head(a, s, 1, vec);
+        } else if (pass == 3) {
+            vec = 16 / gsz;
+            uintptr_t a[2] = {reinterpret_cast<uintptr_t>(t.grad), reinterpret_cast<uintptr_t>(incoming[i])};
+            int64_t s[2] = {gsz, gsz};
+            head = common_head(a, s, 2, vec);
         } else {
             vec = 4;
             uintptr_t a[5] = {reinterpret_cast<uintptr_t>(t.param), reinterpret_cast<uintptr_t>(t.exp_avg),

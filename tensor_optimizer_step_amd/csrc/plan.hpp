@@ -25,6 +25,19 @@ struct alignas(8) Seg1 {
 };
 static_assert(sizeof(Seg1) == 24, "Seg1 layout");
 
+// Device layout of an arrival-pass segment: a contiguous run of one trainable
+// gradient and of the buffer whose values arrive for it.
+struct alignas(16) Seg3 {
+    void* g;            // gradient, rewritten by the pass
+    const void* inc;    // arriving values (same dtype and element order)
+    uint32_t head;      // scalar elements before the first 16-byte vector
+    uint32_t nvec;      // 16-byte vectors of both buffers
+    uint32_t tail;      // scalar elements after the last vector
+    uint16_t dtype;     // gradient somaopt_dtype
+    uint16_t owner;     // 1: the segment enters the sum of squares
+};
+static_assert(sizeof(Seg3) == 32, "Seg3 layout");
+
 // Device layout of an update-pass segment: the same run of p, m, v, g and the
 // optional low-precision working copy.
 struct alignas(16) Seg2 {
@@ -80,9 +93,17 @@ struct Counts {
 int validate_host(const somaopt_tensor_desc* d, int64_t n, int32_t n_groups, std::string& err,
                   Counts* counts);
 
-// pass = 1 (owned gradient segments) or 2 (all trainable segments).
+// Validation of the arriving-gradient buffers of an arrival pass: for every
+// trainable tensor with numel > 0, incoming[i] is non-NULL and aligned to the
+// gradient's element size; the pass writes the gradients, so gradients must not
+// overlap one another nor any p, m, v or working copy, and no arriving buffer
+// may overlap a written buffer (arriving buffers may overlap each other).
+int validate_arrival(const somaopt_tensor_desc* d, int64_t n, const void* const* incoming, std::string& err);
+
+// pass = 1 (owned gradient segments), 2 (all trainable segments, aligned for
+// p/m/v/g) or 3 (all trainable segments, aligned for g and incoming[i]).
 Plan build_plan(const somaopt_tensor_desc* d, int64_t n, int pass, int64_t chunk,
-                int64_t segment_cost = kSegmentCost);
+                int64_t segment_cost = kSegmentCost, const void* const* incoming = nullptr);
 
 // Largest update-pass segment: its vector body is addressed with 32-bit byte
 // offsets (16 bytes per 4-element vector) by the buffer instructions.

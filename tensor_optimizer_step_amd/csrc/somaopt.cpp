@@ -39,6 +39,15 @@ struct somaopt_handle {
     double* d_partials = nullptr;
     double* d_partials2 = nullptr;
     DevState* d_state = nullptr;
+    // arrival pass (registered once by somaopt_register_arrival)
+    std::vector<somaopt_tensor_desc> descs;   // the table given at init
+    Seg3* d_seg3 = nullptr;
+    uint32_t* d_blk3 = nullptr;
+    uint32_t nblk3 = 0;
+    uint32_t lds3 = 0;
+    double* d_partials3 = nullptr;
+    double* d_partials3b = nullptr;
+    int64_t pass1_chunk = 0;
     bool pending = false;          // a norm pass opened an update not yet applied
     hipStream_t cap_stream = nullptr;
     hipGraphExec_t exec = nullptr;
@@ -110,11 +119,39 @@ int64_t env_int(const char* name, int64_t dflt) {
     return (end && *end == 0) ? (int64_t)v : dflt;
 }
 
+// `bytes` at `p` must be device memory of `dev` inside one HIP allocation.
+int check_device_range(const void* p, uintptr_t bytes, int dev, const std::string& at) {
+    hipPointerAttribute_t attr;
+    std::memset(&attr, 0, sizeof(attr));
+    hipError_t e = hipPointerGetAttributes(&attr, p);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(SOMAOPT_E_INVALID, at + "not a HIP device pointer");
+    }
+    if (attr.type != hipMemoryTypeDevice || attr.device != dev)
+        return fail(SOMAOPT_E_INVALID, at + "not device memory of the current device");
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    e = hipMemGetAddressRange(&base, &size, const_cast<void*>(p));
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(SOMAOPT_E_INVALID, at + "allocation range unknown to HIP");
+    }
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(base);
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    if (a < lo || a + bytes > lo + size) return fail(SOMAOPT_E_INVALID, at + "runs past the end of its allocation");
+    return SOMAOPT_OK;
+}
+
+bool skip_pointer_check() {
+    const char* skip = std::getenv("SOMAOPT_SKIP_POINTER_CHECK");
+    return skip && std::strcmp(skip, "1") == 0;
+}
+
 // Every trainable buffer must be device memory of `dev` and lie inside one
 // allocation, so that no kernel can address memory it was not given.
 int check_pointers(const somaopt_tensor_desc* d, int64_t n, int dev) {
-    const char* skip = std::getenv("SOMAOPT_SKIP_POINTER_CHECK");
-    if (skip && std::strcmp(skip, "1") == 0) return SOMAOPT_OK;
+    if (skip_pointer_check()) return SOMAOPT_OK;
     static const char* kind[5] = {"param", "exp_avg", "exp_avg_sq", "grad", "param_lowp"};
     for (int64_t i = 0; i < n; ++i) {
         const somaopt_tensor_desc& t = d[i];
@@ -124,27 +161,8 @@ int check_pointers(const somaopt_tensor_desc* d, int64_t n, int dev) {
         const int nbuf = t.param_lowp ? 5 : 4;
         for (int k = 0; k < nbuf; ++k) {
             const std::string at = "tensor " + std::to_string(i) + " " + kind[k] + ": ";
-            hipPointerAttribute_t attr;
-            std::memset(&attr, 0, sizeof(attr));
-            hipError_t e = hipPointerGetAttributes(&attr, ptrs[k]);
-            if (e != hipSuccess) {
-                (void)hipGetLastError();
-                return fail(SOMAOPT_E_INVALID, at + "not a HIP device pointer");
-            }
-            if (attr.type != hipMemoryTypeDevice || attr.device != dev)
-                return fail(SOMAOPT_E_INVALID, at + "not device memory of the current device");
-            hipDeviceptr_t base = nullptr;
-            size_t size = 0;
-            e = hipMemGetAddressRange(&base, &size, const_cast<void*>(ptrs[k]));
-            if (e != hipSuccess) {
-                (void)hipGetLastError();
-                return fail(SOMAOPT_E_INVALID, at + "allocation range unknown to HIP");
-            }
-            const uintptr_t lo = reinterpret_cast<uintptr_t>(base);
-            const uintptr_t a = reinterpret_cast<uintptr_t>(ptrs[k]);
-            const uintptr_t bytes = (uintptr_t)t.numel * esz[k];
-            if (a < lo || a + bytes > lo + size)
-                return fail(SOMAOPT_E_INVALID, at + "runs past the end of its allocation");
+            int rc = check_device_range(ptrs[k], (uintptr_t)t.numel * esz[k], dev, at);
+            if (rc) return rc;
         }
     }
     return SOMAOPT_OK;
@@ -154,7 +172,9 @@ void free_handle(somaopt_handle* h) {
     if (!h) return;
     if (h->exec) (void)hipGraphExecDestroy(h->exec);
     if (h->cap_stream) (void)hipStreamDestroy(h->cap_stream);
-    void* bufs[] = {h->d_seg1, h->d_blk1, h->d_seg2, h->d_blk2, h->d_partials, h->d_partials2, h->d_state};
+    void* bufs[] = {h->d_seg1,     h->d_blk1,     h->d_seg2,        h->d_blk2,         h->d_partials,
+                    h->d_partials2, h->d_state, h->d_seg3,        h->d_blk3,         h->d_partials3,
+                    h->d_partials3b};
     for (void* p : bufs)
         if (p) (void)hipFree(p);
     delete h;
@@ -336,6 +356,8 @@ int somaopt_init_tensor_table(const somaopt_tensor_desc* descs, int64_t n_tensor
     if (!h) return fail(SOMAOPT_E_NOMEM, "host allocation failed");
     h->device = dev;
     h->n_groups = n_groups;
+    h->descs.assign(descs, descs + n_tensors);
+    h->pass1_chunk = ch1;
     fill_info(&h->info, n_tensors, counts, p1, p2);
     h->nblk1 = (uint32_t)(p1.block_first.size() - 1);
     h->nblk2 = (uint32_t)p2.n_blocks();
@@ -395,6 +417,91 @@ int somaopt_fused_adamw_step(somaopt_handle* h, void* stream) {
     int rc = launch_update_pass(h, static_cast<hipStream_t>(stream));
     if (rc) return rc;
     h->pending = false;
+    return SOMAOPT_OK;
+}
+
+int somaopt_register_arrival(somaopt_handle* h, const void* const* incoming, int64_t n_tensors, void* stream) {
+    if (!h) return fail(SOMAOPT_E_INVALID, "handle is NULL");
+    if (h->d_seg3) return fail(SOMAOPT_E_STATE, "arriving buffers are already registered for this handle");
+    if (n_tensors != (int64_t)h->descs.size())
+        return fail(SOMAOPT_E_INVALID, "n_tensors differs from the table given at init");
+    DeviceGuard g(h->device);
+    if (!g.ok()) return fail(SOMAOPT_E_HIP, "cannot select the handle's device");
+    const somaopt_tensor_desc* d = h->descs.data();
+    std::string err;
+    if (validate_arrival(d, n_tensors, incoming, err) != SOMAOPT_OK) return fail(SOMAOPT_E_INVALID, err);
+    if (!skip_pointer_check()) {
+        for (int64_t i = 0; i < n_tensors; ++i) {
+            if (!d[i].trainable || d[i].numel == 0) continue;
+            int rc = check_device_range(incoming[i], (uintptr_t)d[i].numel * grad_elem_bytes(d[i].grad_dtype),
+                                        h->device, "tensor " + std::to_string(i) + " incoming: ");
+            if (rc) return rc;
+        }
+    }
+    Plan p3 = build_plan(d, n_tensors, 3, h->pass1_chunk, kSegmentCost, incoming);
+    if (p3.segs.size() >= 0xFFFFFFFFull || (uint64_t)p3.n_blocks() * kPass1Threads >= 0xFFFFFFFFull)
+        return fail(SOMAOPT_E_INVALID, "arrival table too large for one dispatch");
+    if (p3.block_first.size() < 2) p3.block_first = {0u, 0u};   // statistics even when nothing is trainable
+    std::vector<Seg3> s3(p3.segs.size());
+    for (size_t i = 0; i < p3.segs.size(); ++i) {
+        const PlanSeg& sg = p3.segs[i];
+        const somaopt_tensor_desc& t = d[sg.tensor];
+        const size_t gsz = (size_t)grad_elem_bytes(t.grad_dtype);
+        s3[i].g = static_cast<char*>(const_cast<void*>(t.grad)) + (size_t)sg.offset * gsz;
+        s3[i].inc = static_cast<const char*>(incoming[sg.tensor]) + (size_t)sg.offset * gsz;
+        s3[i].head = (uint32_t)sg.head;
+        s3[i].nvec = (uint32_t)sg.nvec;
+        s3[i].tail = (uint32_t)sg.tail;
+        s3[i].dtype = (uint16_t)t.grad_dtype;
+        s3[i].owner = (uint16_t)(t.owner ? 1 : 0);
+    }
+    const uint32_t nblk = (uint32_t)(p3.block_first.size() - 1);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if ((e = alloc_upload(&h->d_seg3, s3, s)) != hipSuccess ||
+        (e = alloc_upload(&h->d_blk3, p3.block_first, s)) != hipSuccess ||
+        (e = hipMalloc(reinterpret_cast<void**>(&h->d_partials3), sizeof(double) * nblk)) != hipSuccess ||
+        (e = hipMalloc(reinterpret_cast<void**>(&h->d_partials3b),
+                       sizeof(double) * ((nblk + kReduceSpan - 1) / kReduceSpan + 1))) != hipSuccess ||
+        (e = hipStreamSynchronize(s)) != hipSuccess) {
+        void* bufs[] = {h->d_seg3, h->d_blk3, h->d_partials3, h->d_partials3b};
+        for (void* p : bufs)
+            if (p) (void)hipFree(p);
+        h->d_seg3 = nullptr;
+        h->d_blk3 = nullptr;
+        h->d_partials3 = h->d_partials3b = nullptr;
+        return e == hipErrorOutOfMemory ? fail(SOMAOPT_E_NOMEM, "device allocation of the arrival table failed")
+                                        : hip_fail(e, "arrival table upload");
+    }
+    h->nblk3 = nblk;
+    int lds_per_cu = 0;
+    if (hipDeviceGetAttribute(&lds_per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, h->device) !=
+        hipSuccess)
+        lds_per_cu = 0;
+    h->lds3 = occupancy_lds(lds_per_cu, streaming_plan(p3) ? kPass1WgPerCuStreaming : 0);
+    return SOMAOPT_OK;
+}
+
+int somaopt_arrival_sqnorm(somaopt_handle* h, int32_t accumulate, void* stream) {
+    if (!h) return fail(SOMAOPT_E_INVALID, "handle is NULL");
+    if (!h->d_seg3) return fail(SOMAOPT_E_STATE, "somaopt_register_arrival must precede the arrival pass");
+    if (accumulate != 0 && accumulate != 1) return fail(SOMAOPT_E_INVALID, "accumulate must be 0 or 1");
+    DeviceGuard g(h->device);
+    if (!g.ok()) return fail(SOMAOPT_E_HIP, "cannot select the handle's device");
+    Pass3Args a;
+    a.segs = h->d_seg3;
+    a.blk_first = h->d_blk3;
+    a.n_blocks = h->nblk3;
+    a.partials = h->d_partials3;
+    a.partials2 = h->d_partials3b;
+    a.state = h->d_state;
+    a.n_groups = h->n_groups;
+    a.advance = h->pending ? 0 : 1;
+    a.accumulate = accumulate;
+    a.lds_bytes = h->lds3;
+    hipError_t e = launch_pass3(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "arrival pass launch");
+    h->pending = true;
     return SOMAOPT_OK;
 }
 

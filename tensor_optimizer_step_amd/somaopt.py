@@ -104,6 +104,8 @@ SIGNATURES = {
                                                 _P]),
     "somaopt_attn_ctx_backward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                                  ctypes.POINTER(AttnCtxShape), _P]),
+    "somaopt_register_arrival": (ctypes.c_int, [_P, _PP, ctypes.c_int64, _P]),
+    "somaopt_arrival_sqnorm": (ctypes.c_int, [_P, ctypes.c_int32, _P]),
     "somaopt_destroy": (None, [_P]),
     "somaopt_last_error": (ctypes.c_char_p, []),
     "somaopt_version": (ctypes.c_char_p, []),
@@ -255,6 +257,21 @@ class FusedAdamW:
     # -- step path ---------------------------------------------------------
     def grad_sqnorm(self, stream=None) -> None:
         _check(self._lib.somaopt_grad_sqnorm(self._h, _stream_ptr(stream)))
+
+    def register_arrival(self, incoming: Sequence, stream=None) -> None:
+        """Register the buffers whose values arrive for each tensor's gradient
+        (same shape and dtype; None for frozen tensors).  They must stay alive
+        and in place while the handle lives."""
+        n = len(incoming)
+        arr = (ctypes.c_void_p * max(n, 1))()
+        for i, t in enumerate(incoming):
+            arr[i] = None if t is None else t.data_ptr()
+        self._keep.append(tuple(incoming))
+        _check(self._lib.somaopt_register_arrival(self._h, arr, n, _stream_ptr(stream)))
+
+    def arrival_sqnorm(self, accumulate: bool, stream=None) -> None:
+        """grad <- incoming (or grad + incoming), fused with the norm pass."""
+        _check(self._lib.somaopt_arrival_sqnorm(self._h, int(bool(accumulate)), _stream_ptr(stream)))
 
     def fused_adamw_step(self, stream=None) -> None:
         _check(self._lib.somaopt_fused_adamw_step(self._h, _stream_ptr(stream)))
