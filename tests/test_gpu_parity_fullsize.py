@@ -246,3 +246,61 @@ def test_sharded_7b_full_size_sampled():
                 other = sp[q.shard][q.s_offset:q.s_offset + t.numel]
                 assert torch.equal(ref, other), f"replica of tensor {i} diverged"
     opt.close()
+
+
+def test_action_expert_arrival_full_size():
+    """The 302,092,288-element action expert fed by the arrival pass (the
+    bench's --arrival configuration): three steps alternating accumulate and
+    copy.  The new gradients are compared bit for bit in full against the
+    oracle's accumulation of the host copies, the norm against the oracle's
+    sum over all of them, and p, m, v on sampled windows."""
+    import oracle as O
+    from tensor_optimizer_step_amd.somaopt import FusedAdamW
+    wl = W.action_expert()
+    log(f"[fullsize] arrival {wl.name}: {wl.n_tensors} tensors, {wl.trainable_numel} elements")
+    rng = np.random.default_rng(11)
+    dev = "cuda"
+    p, g, m, v, inc = [], [], [], [], []
+    for i, t in enumerate(wl.tensors):
+        p.append(W.param_values(wl, i, dev))
+        g.append(W.grad_values(wl, i, 1, dev))
+        m.append(torch.zeros(t.numel, device=dev))
+        v.append(torch.zeros(t.numel, device=dev))
+        inc.append(torch.empty_like(g[-1]))
+    idx = [sample_indices(t.numel, rng) for t in wl.tensors]
+    ora = SampledOracle(wl, [_gather(x, ix).numpy() for x, ix in zip(p, idx)], idx)
+    opt = FusedAdamW(p, g, m, v, [t.group for t in wl.tensors], wl.groups, wl.max_norm, wl.grad_divisor)
+    opt.register_arrival(inc)
+    held = [W.to_numpy_grad(x) for x in g]
+    for k, acc in ((1, True), (2, False), (3, True)):
+        for i in range(wl.n_tensors):
+            inc[i].copy_(W.grad_values(wl, i, 20 + k, dev))
+        hin = [W.to_numpy_grad(x) for x in inc]
+        lrs = wl.lrs_for_step(k)
+        opt.set_lrs(lrs)
+        opt.arrival_sqnorm(acc)
+        opt.fused_adamw_step()
+        stats, steps = opt.read_stats()
+        with ThreadPoolExecutor(WORKERS) as ex:
+            new = list(ex.map(lambda i: O.accumulate_gradient(held[i], hin[i], acc), range(wl.n_tensors)))
+        for i in range(wl.n_tensors):
+            assert np.array_equal(W.to_numpy_grad(g[i]), new[i]), f"step {k}: gradient {i} differs"
+        with ThreadPoolExecutor(WORKERS) as ex:
+            parts = list(ex.map(lambda x: O.normalized_sumsq([x], [True], wl.grad_divisor), new))
+        sumsq = 0.0
+        for x in parts:
+            sumsq += x
+        norm, coef = ora.step([x[ix] for x, ix in zip(new, idx)], sumsq, lrs)
+        assert_norm(stats.norm, norm)
+        assert stats.clip_coef == pytest.approx(coef, rel=1e-12)
+        assert steps == [k] * len(wl.groups)
+        log(f"[fullsize] arrival step {k} ({'accumulate' if acc else 'copy'}): norm {stats.norm:.6g}")
+        held = new
+    torch.cuda.synchronize()
+    worst = [0.0, 0.0, 0.0]
+    for i in range(wl.n_tensors):
+        for j, (dev_t, want) in enumerate(((p[i], ora.p[i]), (m[i], ora.m[i]), (v[i], ora.v[i]))):
+            worst[j] = max(worst[j], assert_close(f"{'pmv'[j]}[{i}]", _gather(dev_t, idx[i]).numpy(), want))
+    log(f"[fullsize] arrival: tensor-wise rel err p={worst[0]:.2e} m={worst[1]:.2e} v={worst[2]:.2e}")
+    opt.close()
+    del p, g, m, v, inc
