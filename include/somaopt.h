@@ -250,9 +250,14 @@ int somaopt_set_step(somaopt_handle* h, int64_t step, void* stream);
  * (captured on a private stream; nothing runs).  Replaces an earlier graph. */
 int somaopt_capture_step(somaopt_handle* h);
 
-/* Launch the captured step on `stream`: one full step (norm pass with its
- * step advance, then update pass).  SOMAOPT_E_STATE if not captured or if an
- * eager norm pass is pending. */
+/* Capture {arrival pass with the fused norm, update pass} instead -- the step
+ * of somaopt_arrival_sqnorm(accumulate) followed by somaopt_fused_adamw_step.
+ * Replaces an earlier graph.  SOMAOPT_E_STATE before somaopt_register_arrival. */
+int somaopt_capture_arrival_step(somaopt_handle* h, int32_t accumulate);
+
+/* Launch the captured step on `stream`: one full step (norm or arrival pass
+ * with its step advance, then update pass).  SOMAOPT_E_STATE if not captured
+ * or if an eager norm pass is pending. */
 int somaopt_replay_step(somaopt_handle* h, void* stream);
 
 /* Device address of the somaopt_stats block (valid for the handle's life). */

@@ -241,6 +241,10 @@ int launch_update_pass(somaopt_handle* h, hipStream_t s) {
 
 int somaopt::set_error(int code, const std::string& msg) { return fail(code, msg); }
 
+namespace {
+int launch_arrival_pass(somaopt_handle* h, int advance, int32_t accumulate, hipStream_t s);
+}  // namespace
+
 extern "C" {
 
 const char* somaopt_last_error(void) { return g_last_error.c_str(); }
@@ -488,19 +492,8 @@ int somaopt_arrival_sqnorm(somaopt_handle* h, int32_t accumulate, void* stream) 
     if (accumulate != 0 && accumulate != 1) return fail(SOMAOPT_E_INVALID, "accumulate must be 0 or 1");
     DeviceGuard g(h->device);
     if (!g.ok()) return fail(SOMAOPT_E_HIP, "cannot select the handle's device");
-    Pass3Args a;
-    a.segs = h->d_seg3;
-    a.blk_first = h->d_blk3;
-    a.n_blocks = h->nblk3;
-    a.partials = h->d_partials3;
-    a.partials2 = h->d_partials3b;
-    a.state = h->d_state;
-    a.n_groups = h->n_groups;
-    a.advance = h->pending ? 0 : 1;
-    a.accumulate = accumulate;
-    a.lds_bytes = h->lds3;
-    hipError_t e = launch_pass3(a, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "arrival pass launch");
+    int rc = launch_arrival_pass(h, h->pending ? 0 : 1, accumulate, static_cast<hipStream_t>(stream));
+    if (rc) return rc;
     h->pending = true;
     return SOMAOPT_OK;
 }
@@ -541,8 +534,31 @@ int somaopt_set_step(somaopt_handle* h, int64_t step, void* stream) {
     return SOMAOPT_OK;
 }
 
-int somaopt_capture_step(somaopt_handle* h) {
-    if (!h) return fail(SOMAOPT_E_INVALID, "handle is NULL");
+}  // extern "C"
+
+namespace {
+
+// Arrival pass launch (shared by the eager call and the captured step).
+int launch_arrival_pass(somaopt_handle* h, int advance, int32_t accumulate, hipStream_t s) {
+    Pass3Args a;
+    a.segs = h->d_seg3;
+    a.blk_first = h->d_blk3;
+    a.n_blocks = h->nblk3;
+    a.partials = h->d_partials3;
+    a.partials2 = h->d_partials3b;
+    a.state = h->d_state;
+    a.n_groups = h->n_groups;
+    a.advance = advance;
+    a.accumulate = accumulate;
+    a.lds_bytes = h->lds3;
+    hipError_t e = launch_pass3(a, s);
+    return e == hipSuccess ? SOMAOPT_OK : hip_fail(e, "arrival pass launch");
+}
+
+// Capture {first pass, update pass} on the handle's private stream and make
+// it the handle's step graph.  `arrival` < 0: the norm pass; else the arrival
+// pass with accumulate = arrival.
+int capture(somaopt_handle* h, int arrival) {
     DeviceGuard g(h->device);
     if (!g.ok()) return fail(SOMAOPT_E_HIP, "cannot select the handle's device");
     hipError_t e;
@@ -555,7 +571,7 @@ int somaopt_capture_step(somaopt_handle* h) {
     }
     e = hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeThreadLocal);
     if (e != hipSuccess) return hip_fail(e, "hipStreamBeginCapture");
-    int rc = launch_norm_pass(h, 1, h->cap_stream);
+    int rc = arrival < 0 ? launch_norm_pass(h, 1, h->cap_stream) : launch_arrival_pass(h, 1, arrival, h->cap_stream);
     if (!rc) rc = launch_update_pass(h, h->cap_stream);
     hipGraph_t graph = nullptr;
     e = hipStreamEndCapture(h->cap_stream, &graph);
@@ -571,6 +587,22 @@ int somaopt_capture_step(somaopt_handle* h) {
     if (h->exec) (void)hipGraphExecDestroy(h->exec);
     h->exec = exec;
     return SOMAOPT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int somaopt_capture_step(somaopt_handle* h) {
+    if (!h) return fail(SOMAOPT_E_INVALID, "handle is NULL");
+    return capture(h, -1);
+}
+
+int somaopt_capture_arrival_step(somaopt_handle* h, int32_t accumulate) {
+    if (!h) return fail(SOMAOPT_E_INVALID, "handle is NULL");
+    if (!h->d_seg3) return fail(SOMAOPT_E_STATE, "somaopt_register_arrival must precede the capture");
+    if (accumulate != 0 && accumulate != 1) return fail(SOMAOPT_E_INVALID, "accumulate must be 0 or 1");
+    return capture(h, accumulate);
 }
 
 int somaopt_replay_step(somaopt_handle* h, void* stream) {

@@ -106,6 +106,7 @@ SIGNATURES = {
                                                  ctypes.POINTER(AttnCtxShape), _P]),
     "somaopt_register_arrival": (ctypes.c_int, [_P, _PP, ctypes.c_int64, _P]),
     "somaopt_arrival_sqnorm": (ctypes.c_int, [_P, ctypes.c_int32, _P]),
+    "somaopt_capture_arrival_step": (ctypes.c_int, [_P, ctypes.c_int32]),
     "somaopt_destroy": (None, [_P]),
     "somaopt_last_error": (ctypes.c_char_p, []),
     "somaopt_version": (ctypes.c_char_p, []),
@@ -283,6 +284,10 @@ class FusedAdamW:
 
     def capture(self) -> None:
         _check(self._lib.somaopt_capture_step(self._h))
+
+    def capture_arrival(self, accumulate: bool) -> None:
+        """Capture {arrival pass with the fused norm, update pass} as the step graph."""
+        _check(self._lib.somaopt_capture_arrival_step(self._h, int(bool(accumulate))))
 
     def replay(self, stream=None) -> None:
         _check(self._lib.somaopt_replay_step(self._h, _stream_ptr(stream)))

@@ -190,3 +190,39 @@ def test_arrival_scaled_action_expert_many_workgroups():
         assert_close(f"m[{i}]", host(st.m[i]), ora.m[i])
         assert_close(f"v[{i}]", host(st.v[i]), ora.v[i])
     opt.close()
+
+
+def test_arrival_graph_replay_equals_eager_bitwise():
+    """{arrival, update} captured once and replayed equals the eager calls bit
+    for bit, on two identical states; every replay is checked (several replays
+    with host synchronization between them)."""
+    wl = _workload([W.BF16, W.F32], seed_offset=31, n=30)
+    states, opts, incs = [], [], []
+    for graph in (False, True):
+        st = allocate(wl)
+        fill_grads(wl, st, 1)
+        inc = _incoming(wl, st, False)
+        opt = make_handle(wl, st)
+        opt.register_arrival(inc)
+        if graph:
+            opt.capture_arrival(True)
+        states.append(st)
+        opts.append(opt)
+        incs.append(inc)
+    for k in range(1, 4):
+        for inc in incs:
+            for i, t in enumerate(wl.tensors):
+                if t.trainable:
+                    inc[i].copy_(W.grad_values(wl, i, 60 + k, "cuda"))
+        opts[0].arrival_sqnorm(True)
+        opts[0].fused_adamw_step()
+        opts[1].replay()
+        torch.cuda.synchronize()
+        s0, t0 = opts[0].read_stats()
+        s1, t1 = opts[1].read_stats()
+        assert s0.sumsq == s1.sumsq and t0 == t1 == [k]
+        for name in "pgmv":
+            for a, b in zip(getattr(states[0], name), getattr(states[1], name)):
+                assert np.array_equal(_bits(host(a)), _bits(host(b))), f"replay {k}: {name} differs"
+    for o in opts:
+        o.close()
