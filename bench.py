@@ -47,6 +47,10 @@ def parse():
     ap.add_argument("--arrival", choices=["none", "copy", "accumulate"], default="none",
                     help="time the step as the gradient-arrival pass (copy or accumulate the arriving "
                          "gradients, norm fused in) followed by the update pass")
+    ap.add_argument("--context", action="store_true",
+                    help="also time, for context only, a plain device copy of the update pass's "
+                         "byte count and torch's own clip_grad_norm_ + AdamW(fused=True) on the "
+                         "same shapes (fp32 gradients, which torch's AdamW requires)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for HBM counter scaling)")
     return ap.parse_args()
@@ -88,6 +92,64 @@ def copy_calibration(torch):
     ms = ev0.elapsed_time(ev1) / 10
     print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "ms": ms,
                       "GBps": 8 * n / ms / 1e6}), flush=True)
+
+
+def context_bench(torch, wl, bts: dict, our_ms: float, reps: int = 10) -> dict:
+    """Context numbers on the same GPU, not targets: a plain device copy that
+    moves about as many bytes as the update pass (the runtime's blit kernel),
+    and torch's own step on the same tensor shapes -- clip_grad_norm_ (foreach)
+    followed by AdamW(fused=True) with the same groups -- on fp32 gradients."""
+    from tensor_optimizer_step_amd import workloads as W
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    n = min(bts["pass2"] // 8, 1 << 31)
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    ms_copy = timed(lambda: b.copy_(a))
+    del a, b
+    torch.cuda.empty_cache()
+
+    idx = [i for i, t in enumerate(wl.tensors) if t.trainable]
+    params = [torch.nn.Parameter(W.param_values(wl, i, "cuda")) for i in idx]
+    for p, i in zip(params, idx):
+        p.grad = W.grad_values(wl, i, 1, "cuda").float()
+    groups = []
+    for k, h in enumerate(wl.groups):
+        ps = [p for p, i in zip(params, idx) if wl.tensors[i].group == k]
+        if ps:
+            groups.append({"params": ps, "lr": h.lr, "weight_decay": h.weight_decay,
+                           "betas": (h.beta1, h.beta2), "eps": h.eps})
+    try:
+        opt = torch.optim.AdamW(groups, fused=True)
+        kind = "fused"
+    except (RuntimeError, ValueError):
+        opt = torch.optim.AdamW(groups, foreach=True)
+        kind = "foreach"
+
+    def torch_step():
+        torch.nn.utils.clip_grad_norm_(params, wl.max_norm, foreach=True)
+        opt.step()
+    ms_torch = timed(torch_step)
+    n_elem = sum(p.numel() for p in params)
+    del opt, params, groups
+    torch.cuda.empty_cache()
+    return {"plain_copy": {"bytes_moved": 8 * n, "ms": round(ms_copy, 5),
+                           "GBps": round(8 * n / ms_copy / 1e6, 1)},
+            "torch_step": {"ops": f"clip_grad_norm_(foreach) + AdamW({kind})", "grad_dtype": "f32",
+                           "ms_per_step": round(ms_torch, 5),
+                           "elements_per_s": n_elem / (ms_torch * 1e-3),
+                           "this_path_speedup": round(ms_torch / our_ms, 2)}}
 
 
 def cpu_baseline(wl, seconds: float) -> dict:
@@ -482,6 +544,9 @@ def main():
     }
     opt.close()
     del keep
+    if args.context:
+        torch.cuda.empty_cache()
+        out["context"] = context_bench(torch, wl, bts, step_s * 1e3)
     print(json.dumps(out), flush=True)
 
 
