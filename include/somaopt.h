@@ -4,7 +4,7 @@
  * What the library computes (SomaSpeed landing page, prose paragraphs 7 and 8,
  * numbered in page order after the title: the post-backward optimizer work and
  * its fused form): after backward, over a table of many trainable tensors,
- *   1. normalize the gradients for the effective batch (divide by D),
+ *   1. divide every gradient by the effective-batch divisor D,
  *   2. measure one global L2 norm in which every owned gradient element counts
  *      once,
  *   3. take one global clip decision  c = min(1, max_norm / (norm + 1e-6))
@@ -234,8 +234,8 @@ int somaopt_arrival_sqnorm(somaopt_handle* h, int32_t accumulate, void* stream);
 
 /* Replace every group's hyperparameters (n_groups must equal the handle's).
  * Enqueued as a tiny kernel whose arguments carry the values, so the host
- * array may be reused at once; a learning-rate schedule calls this before
- * each step ("learning-rate schedules retain their configured behavior"). */
+ * array may be reused at once; a learning-rate schedule computed on the host
+ * calls this before each step, so every group keeps its own schedule. */
 int somaopt_set_groups(somaopt_handle* h, const somaopt_group* groups, int32_t n_groups,
                        void* stream);
 
