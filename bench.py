@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--arrival", choices=["none", "copy", "accumulate"], default="none",
                     help="time the step as the gradient-arrival pass (copy or accumulate the arriving "
                          "gradients, norm fused in) followed by the update pass")
+    ap.add_argument("--host-schedule", action="store_true",
+                    help="scheduled workloads: set each step's lr from the host before the replay "
+                         "instead of evaluating the schedule on the device")
     ap.add_argument("--context", action="store_true",
                     help="also time, for context only, a plain device copy of the update pass's "
                          "byte count and torch's own clip_grad_norm_ + AdamW(fused=True) on the "
@@ -195,6 +198,15 @@ def load_traffic(workload: str, algo_bytes: int):
     if rec.get("kernel_sha256_16") != kernel_hash():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def device_schedules(somaopt, wl):
+    """The workload's per-group lr schedule as on-device schedules."""
+    if wl.schedule == "warmup":
+        return [(somaopt.SCHED_LINEAR_WARMUP, wl.steps, 0, g.lr, 0.0) for g in wl.groups]
+    if wl.schedule == "cosine":
+        return [(somaopt.SCHED_COSINE, 0, wl.steps, g.lr, 0.0) for g in wl.groups]
+    raise ValueError(f"no device form for schedule {wl.schedule!r}")
 
 
 def plain_setup(torch, somaopt, W, wl, dev, stream, lowp_dtype):
@@ -472,15 +484,22 @@ def main():
         arrival_bench(torch, args, wl, opt, keep, stream, bts)
         return
 
+    # The workload's lr schedule: evaluated on the device by the captured step
+    # itself (set once), or with --host-schedule by a setter call before each
+    # replay.  Constant schedules need neither.
+    host_sched = wl.schedule != "constant" and args.host_schedule
+    if wl.schedule != "constant" and not args.host_schedule:
+        opt.set_schedules(device_schedules(somaopt, wl), stream)
+
     # warm-up, then exactly K timed replays of the captured step
     for k in range(args.warmup):
-        opt.set_lrs(wl.lrs_for_step(1 + k % wl.steps), stream)
+        if host_sched:
+            opt.set_lrs(wl.lrs_for_step(1 + k % wl.steps), stream)
         opt.replay(stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    scheduled = wl.schedule != "constant"
     for k in range(args.steps):
-        if scheduled:
+        if host_sched:
             opt.set_lrs(wl.lrs_for_step(1 + k % wl.steps), stream)
         opt.replay(stream)
     torch.cuda.synchronize()
@@ -538,7 +557,10 @@ def main():
                    "grad_dtype": wl.tensors[0].grad_dtype, "state_dtype": "f32",
                    "model_bytes_per_step": bts["total"], "groups": len(wl.groups),
                    "pass1_blocks": info.pass1_blocks, "pass2_blocks": info.pass2_blocks,
-                   "graph": True, "working_copy": args.lowp},
+                   "graph": True, "working_copy": args.lowp,
+                   "lr_schedule": wl.schedule + ("" if wl.schedule == "constant" else
+                                                 (", host setter per step" if args.host_schedule
+                                                  else ", on device"))},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -239,6 +239,40 @@ int somaopt_arrival_sqnorm(somaopt_handle* h, int32_t accumulate, void* stream);
 int somaopt_set_groups(somaopt_handle* h, const somaopt_group* groups, int32_t n_groups,
                        void* stream);
 
+/* Learning-rate schedules evaluated on the device (optional; landing page,
+ * paragraph 8: every parameter group keeps its own schedule).  A group with
+ * a schedule takes, for its update t (1 on the first update), the lr below in
+ * place of somaopt_group.lr; its other hyperparameters still come from init
+ * or somaopt_set_groups.  The finalize of the norm (or arrival) pass computes
+ * the lr in fp64 together with the bias corrections, so a captured step
+ * replays the whole schedule with no host call between steps.  With
+ * W = warmup, T = total, peak = peak_lr, floor = floor_lr:
+ *   SOMAOPT_SCHED_NONE           lr = somaopt_group.lr (the default)
+ *   SOMAOPT_SCHED_LINEAR_WARMUP  lr = peak * min(t, W) / W
+ *   SOMAOPT_SCHED_COSINE         lr = floor + (peak - floor) * (1 + cos(pi * k / T)) / 2,
+ *                                k = min(t - 1, T): peak at t = 1, floor from t = T + 1
+ *   SOMAOPT_SCHED_WARMUP_COSINE  t <= W: the linear warmup; t > W: the cosine over
+ *                                the remaining T - W updates (k = min(t - W - 1, T - W))
+ * The new schedules apply from the next norm or arrival pass.  Errors
+ * (SOMAOPT_E_INVALID): n_groups differs from the handle's, an unknown kind,
+ * W < 1 for a warmup kind, T < 1 for a cosine kind, T <= W for warmup-cosine,
+ * or a peak or floor lr that is negative or not finite. */
+typedef enum {
+    SOMAOPT_SCHED_NONE = 0,
+    SOMAOPT_SCHED_LINEAR_WARMUP = 1,
+    SOMAOPT_SCHED_COSINE = 2,
+    SOMAOPT_SCHED_WARMUP_COSINE = 3
+} somaopt_schedule_kind;
+typedef struct {
+    int32_t kind;      /* somaopt_schedule_kind */
+    int32_t warmup;    /* W */
+    int64_t total;     /* T */
+    double peak_lr;
+    double floor_lr;
+} somaopt_schedule;
+int somaopt_set_schedules(somaopt_handle* h, const somaopt_schedule* schedules, int32_t n_groups,
+                          void* stream);
+
 /* Replace max_norm and grad_divisor (both > 0), stream ordered. */
 int somaopt_set_clip(somaopt_handle* h, double max_norm, double grad_divisor, void* stream);
 

@@ -9,3 +9,4 @@ from .adamw_fp64 import (CLIP_EPS, Group, Oracle, StepStats, adamw_update,  # no
 from .attention_fp64 import (attention_backward, attention_forward, attention_probs,  # noqa: F401
                              error_budget_backward, error_budget_forward)
 from .accumulate_fp64 import accumulate_gradient  # noqa: F401
+from .schedule_fp64 import scheduled_lr  # noqa: F401

@@ -230,6 +230,22 @@ __device__ __forceinline__ double int_pow(double b, int64_t t) {
     return r;
 }
 
+// The learning rate of update t under an on-device schedule (fp64); `lr` is
+// the group's own value, used when the group has none.  The definitions are
+// those of somaopt_set_schedules.
+__device__ double scheduled_lr(const somaopt_schedule& s, int64_t t, double lr) {
+    if (s.kind == SOMAOPT_SCHED_NONE) return lr;
+    const int64_t w = s.kind == SOMAOPT_SCHED_COSINE ? 0 : s.warmup;
+    if (s.kind == SOMAOPT_SCHED_LINEAR_WARMUP || t <= w) {
+        const int64_t tt = t < w ? (t < 0 ? 0 : t) : w;
+        return s.peak_lr * (double)tt / (double)w;
+    }
+    const int64_t span = s.total - w;
+    int64_t k = t - w - 1;
+    k = k < 0 ? 0 : (k > span ? span : k);
+    return s.floor_lr + (s.peak_lr - s.floor_lr) * 0.5 * (1.0 + cos(M_PI * (double)k / (double)span));
+}
+
 // Group k's update count and bias-corrected constants (fp64, rounded once).
 __device__ void finalize_group(DevState* st, int k, int advance) {
     int64_t t = st->step[k];
@@ -238,12 +254,13 @@ __device__ void finalize_group(DevState* st, int k, int advance) {
         st->step[k] = t;
     }
     const somaopt_group h = st->hyper[k];
+    const double lr = scheduled_lr(st->sched[k], t, h.lr);
     const double bc1 = 1.0 - int_pow(h.beta1, t);
     const double bc2 = 1.0 - int_pow(h.beta2, t);
     GroupConst c;
-    c.step_size = (float)(h.lr / bc1);
+    c.step_size = (float)(lr / bc1);
     c.inv_sqrt_bc2 = (float)(1.0 / sqrt(bc2));
-    c.lr_wd = (float)(h.lr * h.weight_decay);
+    c.lr_wd = (float)(lr * h.weight_decay);
     c.beta1 = (float)h.beta1;
     c.one_minus_beta1 = (float)(1.0 - h.beta1);
     c.beta2 = (float)h.beta2;
@@ -639,6 +656,11 @@ __global__ void set_groups_kernel(DevState* st, GroupArgs g) {
     if (k < g.n) st->hyper[k] = g.g[k];
 }
 
+__global__ void set_schedules_kernel(DevState* st, ScheduleArgs a) {
+    const int k = threadIdx.x;
+    if (k < a.n) st->sched[k] = a.s[k];
+}
+
 __global__ void set_clip_kernel(DevState* st, double max_norm, double grad_divisor) {
     if (threadIdx.x == 0) {
         st->max_norm = max_norm;
@@ -698,6 +720,11 @@ hipError_t launch_pass2(const Pass2Args& a, hipStream_t s) {
 
 hipError_t launch_set_groups(DevState* st, const GroupArgs& g, hipStream_t s) {
     hipLaunchKernelGGL(set_groups_kernel, dim3(1), dim3(SOMAOPT_MAX_GROUPS), 0, s, st, g);
+    return hipGetLastError();
+}
+
+hipError_t launch_set_schedules(DevState* st, const ScheduleArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL(set_schedules_kernel, dim3(1), dim3(SOMAOPT_MAX_GROUPS), 0, s, st, a);
     return hipGetLastError();
 }
 

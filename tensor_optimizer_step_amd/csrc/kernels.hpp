@@ -85,6 +85,7 @@ hipError_t launch_pass1(const Pass1Args& a, hipStream_t s);
 hipError_t launch_pass2(const Pass2Args& a, hipStream_t s);
 hipError_t launch_pass3(const Pass3Args& a, hipStream_t s);
 hipError_t launch_set_groups(DevState* st, const GroupArgs& g, hipStream_t s);
+hipError_t launch_set_schedules(DevState* st, const ScheduleArgs& a, hipStream_t s);
 hipError_t launch_set_clip(DevState* st, double max_norm, double grad_divisor, hipStream_t s);
 hipError_t launch_set_step(DevState* st, int64_t step, int32_t n_groups, hipStream_t s);
 

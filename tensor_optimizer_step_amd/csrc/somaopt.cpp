@@ -513,6 +513,36 @@ int somaopt_set_groups(somaopt_handle* h, const somaopt_group* groups, int32_t n
     return e == hipSuccess ? SOMAOPT_OK : hip_fail(e, "set_groups launch");
 }
 
+int somaopt_set_schedules(somaopt_handle* h, const somaopt_schedule* schedules, int32_t n_groups, void* stream) {
+    if (!h) return fail(SOMAOPT_E_INVALID, "handle is NULL");
+    if (n_groups != h->n_groups) return fail(SOMAOPT_E_INVALID, "n_groups differs from the handle's");
+    if (!schedules) return fail(SOMAOPT_E_INVALID, "schedules is NULL");
+    ScheduleArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.n = n_groups;
+    for (int32_t k = 0; k < n_groups; ++k) {
+        const somaopt_schedule& c = schedules[k];
+        const std::string at = "schedule " + std::to_string(k) + ": ";
+        if (c.kind < SOMAOPT_SCHED_NONE || c.kind > SOMAOPT_SCHED_WARMUP_COSINE)
+            return fail(SOMAOPT_E_INVALID, at + "unknown kind");
+        if (c.kind != SOMAOPT_SCHED_NONE) {
+            if (!(c.peak_lr >= 0.0) || !std::isfinite(c.peak_lr) || !(c.floor_lr >= 0.0) || !std::isfinite(c.floor_lr))
+                return fail(SOMAOPT_E_INVALID, at + "peak_lr and floor_lr must be finite and >= 0");
+            const bool warm = c.kind == SOMAOPT_SCHED_LINEAR_WARMUP || c.kind == SOMAOPT_SCHED_WARMUP_COSINE;
+            const bool cosine = c.kind == SOMAOPT_SCHED_COSINE || c.kind == SOMAOPT_SCHED_WARMUP_COSINE;
+            if (warm && c.warmup < 1) return fail(SOMAOPT_E_INVALID, at + "warmup must be >= 1");
+            if (cosine && c.total < 1) return fail(SOMAOPT_E_INVALID, at + "total must be >= 1");
+            if (c.kind == SOMAOPT_SCHED_WARMUP_COSINE && c.total <= c.warmup)
+                return fail(SOMAOPT_E_INVALID, at + "total must exceed warmup");
+        }
+        a.s[k] = c;
+    }
+    DeviceGuard g(h->device);
+    if (!g.ok()) return fail(SOMAOPT_E_HIP, "cannot select the handle's device");
+    hipError_t e = launch_set_schedules(h->d_state, a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SOMAOPT_OK : hip_fail(e, "set_schedules launch");
+}
+
 int somaopt_set_clip(somaopt_handle* h, double max_norm, double grad_divisor, void* stream) {
     if (!h) return fail(SOMAOPT_E_INVALID, "handle is NULL");
     int rc = check_clip(max_norm, grad_divisor);

@@ -30,6 +30,7 @@ struct DevState {
     int64_t step[SOMAOPT_MAX_GROUPS];         // completed (or pending) updates per group
     somaopt_group hyper[SOMAOPT_MAX_GROUPS];  // current hyperparameters
     GroupConst gconst[SOMAOPT_MAX_GROUPS];    // constants of the pending update
+    somaopt_schedule sched[SOMAOPT_MAX_GROUPS];   // on-device lr schedules (kind 0: none)
 };
 
 // Kernel-argument carrier for somaopt_set_groups (passed by value).
@@ -37,6 +38,13 @@ struct GroupArgs {
     int32_t n;
     int32_t pad;
     somaopt_group g[SOMAOPT_MAX_GROUPS];
+};
+
+// Kernel-argument carrier for somaopt_set_schedules (passed by value).
+struct ScheduleArgs {
+    int32_t n;
+    int32_t pad;
+    somaopt_schedule s[SOMAOPT_MAX_GROUPS];
 };
 
 }  // namespace somaopt

@@ -39,6 +39,14 @@ class Group(ctypes.Structure):
                 ("eps", ctypes.c_double)]
 
 
+SCHED_NONE, SCHED_LINEAR_WARMUP, SCHED_COSINE, SCHED_WARMUP_COSINE = 0, 1, 2, 3
+
+
+class Schedule(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("warmup", ctypes.c_int32), ("total", ctypes.c_int64),
+                ("peak_lr", ctypes.c_double), ("floor_lr", ctypes.c_double)]
+
+
 class Stats(ctypes.Structure):
     _fields_ = [("sumsq", ctypes.c_double), ("norm", ctypes.c_double),
                 ("clip_coef", ctypes.c_double), ("grad_scale", ctypes.c_double),
@@ -85,6 +93,7 @@ SIGNATURES = {
     "somaopt_grad_sqnorm": (ctypes.c_int, [_P, _P]),
     "somaopt_fused_adamw_step": (ctypes.c_int, [_P, _P]),
     "somaopt_set_groups": (ctypes.c_int, [_P, ctypes.POINTER(Group), ctypes.c_int32, _P]),
+    "somaopt_set_schedules": (ctypes.c_int, [_P, ctypes.POINTER(Schedule), ctypes.c_int32, _P]),
     "somaopt_set_clip": (ctypes.c_int, [_P, ctypes.c_double, ctypes.c_double, _P]),
     "somaopt_set_step": (ctypes.c_int, [_P, ctypes.c_int64, _P]),
     "somaopt_capture_step": (ctypes.c_int, [_P]),
@@ -303,6 +312,18 @@ class FusedAdamW:
         for k, lr in enumerate(lrs):
             g[k].lr = float(lr)
         _check(self._lib.somaopt_set_groups(self._h, g, self.n_groups, _stream_ptr(stream)))
+
+    def set_schedules(self, schedules: Sequence, stream=None) -> None:
+        """On-device lr schedule per group: each entry a dict or tuple
+        (kind, warmup, total, peak_lr, floor_lr); kind SCHED_NONE keeps the
+        group's own lr."""
+        arr = (Schedule * max(len(schedules), 1))()
+        for k, sc in enumerate(schedules):
+            if isinstance(sc, dict):
+                sc = (sc.get("kind", SCHED_NONE), sc.get("warmup", 0), sc.get("total", 0),
+                      sc.get("peak_lr", 0.0), sc.get("floor_lr", 0.0))
+            arr[k] = Schedule(int(sc[0]), int(sc[1]), int(sc[2]), float(sc[3]), float(sc[4]))
+        _check(self._lib.somaopt_set_schedules(self._h, arr, len(schedules), _stream_ptr(stream)))
 
     def set_clip(self, max_norm: float, grad_divisor: float, stream=None) -> None:
         _check(self._lib.somaopt_set_clip(self._h, float(max_norm), float(grad_divisor),

@@ -10,6 +10,7 @@ import math
 import numpy as np
 import pytest
 
+import oracle as O
 from tensor_optimizer_step_amd import workloads as W
 
 from parity_util import (assert_close, assert_norm, allocate, fill_grads, host, log,
@@ -31,8 +32,18 @@ def _gpu():
     torch.cuda.empty_cache()
 
 
-def run_and_compare(wl, steps=None, graph=True, max_norm=None, divisor=None, check_every_step=True):
-    """Run ``steps`` updates on the GPU and the oracle; compare everything."""
+def schedule_lrs(wl, schedules, k):
+    """The oracle's per-group lr of update k under on-device schedules."""
+    return [O.scheduled_lr(sc[0], k, lr=g.lr, peak=sc[3], floor=sc[4], warmup=sc[1], total=sc[2])
+            for sc, g in zip(schedules, wl.groups)]
+
+
+def run_and_compare(wl, steps=None, graph=True, max_norm=None, divisor=None, check_every_step=True,
+                    schedules=None):
+    """Run ``steps`` updates on the GPU and the oracle; compare everything.
+    With ``schedules`` the handle evaluates the lr schedules on the device
+    (set once, no host call between steps) and the oracle follows its own
+    schedule functions."""
     steps = wl.steps if steps is None else steps
     log(f"[parity] {wl.name}: {wl.n_tensors} tensors, {wl.trainable_numel} trainable, "
         f"{steps} steps, graph={graph}")
@@ -46,14 +57,19 @@ def run_and_compare(wl, steps=None, graph=True, max_norm=None, divisor=None, che
     if divisor is not None:
         kw["grad_divisor"] = divisor
     opt = make_handle(wl, st, **kw)
+    if schedules is not None:
+        opt.set_schedules(schedules)
     ora = make_oracle(wl, p0, max_norm=max_norm, divisor=divisor)
     if graph:
         opt.capture()
     for k in range(1, steps + 1):
         fill_grads(wl, st, k)
         grads = [host(g) for g in st.g]
-        lrs = wl.lrs_for_step(k)
-        opt.set_lrs(lrs)
+        if schedules is None:
+            lrs = wl.lrs_for_step(k)
+            opt.set_lrs(lrs)
+        else:
+            lrs = schedule_lrs(wl, schedules, k)
         if graph:
             opt.replay()
         else:
@@ -109,6 +125,84 @@ def test_launch_bound_full_ten_steps():
 
 def test_launch_bound_clipped_variant():
     run_and_compare(W.launch_bound(n_tensors=3000), steps=4, max_norm=1.0)
+
+
+def test_launch_bound_device_warmup_schedule():
+    # the launch-bound warm-up evaluated on the device, past its end
+    from tensor_optimizer_step_amd import somaopt
+    wl = W.launch_bound(n_tensors=3000)
+    scheds = [(somaopt.SCHED_LINEAR_WARMUP, wl.steps, 0, g.lr, 0.0) for g in wl.groups]
+    run_and_compare(wl, steps=wl.steps + 2, schedules=scheds)
+
+
+def test_device_cosine_and_warmup_cosine_schedules():
+    from tensor_optimizer_step_amd import somaopt
+    wl = W.action_expert(blocks=1, d=128, mlp=512, action_dim=16)
+    scheds = [(somaopt.SCHED_COSINE, 0, 6, 2e-4, 1e-5),
+              (somaopt.SCHED_WARMUP_COSINE, 2, 6, 1e-4, 0.0)]
+    run_and_compare(wl, steps=9, schedules=scheds)
+
+
+def test_device_schedule_bitwise_equals_host_setter():
+    """The device's linear warm-up takes the same fp64 operations as the host's
+    schedule, so a replayed step with no host call matches eager steps fed by
+    somaopt_set_groups bit for bit."""
+    from tensor_optimizer_step_amd import somaopt
+    wl = W.launch_bound(n_tensors=500)
+    sts, opts = [], []
+    for device_sched in (False, True):
+        st = allocate(wl)
+        opt = make_handle(wl, st)
+        if device_sched:
+            opt.set_schedules([(somaopt.SCHED_LINEAR_WARMUP, wl.steps, 0, g.lr, 0.0) for g in wl.groups])
+            opt.capture()
+        sts.append(st)
+        opts.append(opt)
+    for k in range(1, 6):
+        for st in sts:
+            fill_grads(wl, st, k)
+        opts[0].set_lrs(wl.lrs_for_step(k))
+        opts[0].step()
+        opts[1].replay()
+    torch.cuda.synchronize()
+    for name in "pmv":
+        for i, (a, b) in enumerate(zip(getattr(sts[0], name), getattr(sts[1], name))):
+            assert np.array_equal(host(a).view(np.uint32), host(b).view(np.uint32)), f"{name}{i}"
+    for o in opts:
+        o.close()
+
+
+def test_schedule_validation_and_reset():
+    from tensor_optimizer_step_amd import somaopt
+    wl = W.tiny(seed_offset=5)
+    st = allocate(wl)
+    opt = make_handle(wl, st)
+    bad = [(7, 1, 1, 1e-3, 0.0), (somaopt.SCHED_LINEAR_WARMUP, 0, 0, 1e-3, 0.0),
+           (somaopt.SCHED_COSINE, 0, 0, 1e-3, 0.0), (somaopt.SCHED_WARMUP_COSINE, 5, 5, 1e-3, 0.0),
+           (somaopt.SCHED_COSINE, 0, 4, -1e-3, 0.0), (somaopt.SCHED_COSINE, 0, 4, math.nan, 0.0),
+           (somaopt.SCHED_COSINE, 0, 4, 1e-3, math.inf)]
+    for sc in bad:
+        with pytest.raises(somaopt.SomaoptError):
+            opt.set_schedules([sc])
+    with pytest.raises(somaopt.SomaoptError):
+        opt.set_schedules([(somaopt.SCHED_NONE, 0, 0, 0.0, 0.0)] * 2)   # wrong group count
+    # a schedule, then back to none: the group's own lr applies again
+    ora = make_oracle(wl, [host(x) for x in st.p])
+    opt.set_schedules([(somaopt.SCHED_COSINE, 0, 3, 1e-4, 0.0)])
+    fill_grads(wl, st, 1)
+    opt.step()
+    ora.step([host(g) for g in st.g], [O.scheduled_lr(O.schedule_fp64.COSINE, 1, peak=1e-4, total=3)])
+    opt.set_schedules([(somaopt.SCHED_NONE, 0, 0, 0.0, 0.0)])
+    fill_grads(wl, st, 2)
+    opt.step()
+    ora.step([host(g) for g in st.g], wl.lrs_for_step(2))
+    torch.cuda.synchronize()
+    for i, t in enumerate(wl.tensors):
+        if t.trainable:
+            assert_close(f"p[{i}]", host(st.p[i]), ora.p[i])
+            assert_close(f"m[{i}]", host(st.m[i]), ora.m[i])
+            assert_close(f"v[{i}]", host(st.v[i]), ora.v[i])
+    opt.close()
 
 
 def test_edge_sizes_and_empty_tensors():
