@@ -486,6 +486,50 @@ def test_working_copy_and_gradient_dtypes(gdt, ldt):
     opt.close()
 
 
+@pytest.mark.parametrize("shift", [0, 4])
+def test_working_copy_odd_vector_counts(shift):
+    """bf16 working copies whose vector bodies hold odd numbers of 4-element
+    vectors (the last vector has no partner for the paired 16-byte store), at
+    a 16-byte-aligned start (shift 0) and at one only 8-byte aligned (shift 4
+    elements: the per-lane 8-byte stores).  Guard elements on both sides of
+    every copy must stay untouched."""
+    import oracle as O
+    from tensor_optimizer_step_amd.somaopt import FusedAdamW
+    sizes = [1, 3, 4, 5, 7, 8, 12, 13, 20, 28, 36, 4092, 4096, 4100, 4104, 8196, 12292, 65540]
+    tensors = [W.TensorSpec(f"w{i}", n, i % 2, W.BF16) for i, n in enumerate(sizes)]
+    wl = W.Workload("lowp_edges", 1, tensors, [W.GroupHP(1e-3, 0.1), W.GroupHP(2e-3, 0.0)],
+                    max_norm=1.0, grad_divisor=2.0, steps=3)
+    log(f"[parity] working copy odd vector counts, shift={shift}")
+    st = allocate(wl)
+    guard = 8
+    arenas = [torch.full((t.numel + shift + guard,), float("nan"), dtype=torch.bfloat16, device="cuda")
+              for t in tensors]
+    lowp = [a[shift:shift + t.numel] for a, t in zip(arenas, tensors)]
+    before = [a.cpu().view(torch.int16).numpy().copy() for a in arenas]
+    p0 = [host(x) for x in st.p]
+    opt = FusedAdamW(st.p, st.g, st.m, st.v, [t.group for t in tensors], wl.groups, wl.max_norm,
+                     wl.grad_divisor, params_lowp=lowp)
+    ora = make_oracle(wl, p0)
+    opt.capture()
+    for k in range(1, wl.steps + 1):
+        fill_grads(wl, st, k)
+        grads = [host(g) for g in st.g]
+        opt.replay()
+        ora.step(grads)
+    torch.cuda.synchronize()
+    for i, t in enumerate(tensors):
+        gp = host(st.p[i])
+        assert_close(f"p[{i}]", gp, ora.p[i])
+        assert_close(f"m[{i}]", host(st.m[i]), ora.m[i])
+        assert_close(f"v[{i}]", host(st.v[i]), ora.v[i])
+        words = arenas[i].cpu().view(torch.int16).numpy()
+        got = words[shift:shift + t.numel].view(np.uint16)
+        assert np.array_equal(got, O.round_to_bf16_bits(gp)), f"working copy {i} (numel {t.numel})"
+        assert np.array_equal(words[:shift], before[i][:shift]), f"guard before copy {i}"
+        assert np.array_equal(words[shift + t.numel:], before[i][shift + t.numel:]), f"guard after copy {i}"
+    opt.close()
+
+
 def test_setters_mid_run_and_side_stream():
     """Change max_norm / divisor and the hyperparameters between steps, reset
     the step count on a live handle, and run everything on a non-default
