@@ -99,7 +99,8 @@ def copy_calibration(torch):
 
 def context_bench(torch, wl, bts: dict, our_ms: float, reps: int = 10) -> dict:
     """Context numbers on the same GPU, not targets: a plain device copy that
-    moves about as many bytes as the update pass (the runtime's blit kernel),
+    moves about as many bytes as the update pass (the runtime's blit kernel), a
+    STREAM triad of the same size through torch's elementwise kernel,
     and torch's own step on the same tensor shapes -- clip_grad_norm_ (foreach)
     followed by AdamW(fused=True) with the same groups -- on fp32 gradients."""
     from tensor_optimizer_step_amd import workloads as W
@@ -121,6 +122,14 @@ def context_bench(torch, wl, bts: dict, our_ms: float, reps: int = 10) -> dict:
     b = torch.empty_like(a)
     ms_copy = timed(lambda: b.copy_(a))
     del a, b
+    torch.cuda.empty_cache()
+    # STREAM triad through torch's elementwise kernel: x = y + s z, 12 B per element
+    nt = min(bts["pass2"] // 12, 1 << 31)
+    x = torch.empty(nt, dtype=torch.float32, device="cuda")
+    y = torch.ones_like(x)
+    z = torch.ones_like(x)
+    ms_triad = timed(lambda: torch.add(y, z, alpha=0.5, out=x))
+    del x, y, z
     torch.cuda.empty_cache()
 
     idx = [i for i, t in enumerate(wl.tensors) if t.trainable]
@@ -149,6 +158,8 @@ def context_bench(torch, wl, bts: dict, our_ms: float, reps: int = 10) -> dict:
     torch.cuda.empty_cache()
     return {"plain_copy": {"bytes_moved": 8 * n, "ms": round(ms_copy, 5),
                            "GBps": round(8 * n / ms_copy / 1e6, 1)},
+            "triad": {"bytes_moved": 12 * nt, "ms": round(ms_triad, 5),
+                      "GBps": round(12 * nt / ms_triad / 1e6, 1), "kernel": "torch.add(out=)"},
             "torch_step": {"ops": f"clip_grad_norm_(foreach) + AdamW({kind})", "grad_dtype": "f32",
                            "ms_per_step": round(ms_torch, 5),
                            "elements_per_s": n_elem / (ms_torch * 1e-3),
