@@ -310,10 +310,33 @@ struct DqLds {
     uint16_t kr[kRows][D + kPadTr];   // the same K tile, read transposed (A of dQ^T)
     uint16_t v[kRows][D + kPadRow];   // V tile, read by rows (A of dP^T)
 };
-
+// With every query of the (batch, head) in the workgroup, the same memory
+// holds, after a trainable tile's dQ products, the workgroup's Q and dO rows
+// (one pitch, read both ways) and their log-sum-exp and delta for the tile's
+// dK and dV.
 template <int D>
+struct DqKvLds {
+    uint16_t q[kRows][D + kPadTr];
+    uint16_t d_o[kRows][D + kPadTr];
+    float lse2[kRows];
+    float delta[kRows];
+};
+template <int D>
+union DqShared {
+    DqLds<D> t;
+    DqKvLds<D> x;
+};
+
+// FUSE_KV (the workgroup holds every query of its (batch, head), i.e.
+// lq <= 64): after the dQ products of each trainable tile, the workgroup also
+// produces that tile's dK and dV -- complete, since no other workgroup holds
+// queries of this (batch, head) -- in place of the separate dK/dV kernel,
+// which would read Q, dO, K and V again.  Wave w takes keys 16 w .. + 15 of the
+// tile; the products are those of attn_bwd_dkdv over the 64 queries.
+template <int D, bool FUSE_KV>
 __global__ __launch_bounds__(kThreads) void attn_bwd_dq(AttnArgs a) {
-    __shared__ DqLds<D> s;
+    __shared__ DqShared<D> su;
+    DqLds<D>& s = su.t;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
     const size_t bh = (size_t)blockIdx.z * a.heads + blockIdx.y;
@@ -341,6 +364,78 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq(AttnArgs a) {
 #pragma unroll
     for (int nb = 0; nb < D / 16; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // dK and dV of one staged trainable tile (FUSE_KV only); key0 is the
+    // tile's first trainable key, bound the trainable key count.
+    auto tile_dkdv = [&](int key0, int bound) {
+        // B operands from the staged tile: K[key][32 kk + 8 g ..], V[key][..]
+        u32x4 kb_[D / 32], vb_[D / 32];
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) {
+            kb_[kk] = *reinterpret_cast<const u32x4*>(&s.k[16 * w + r][32 * kk + 8 * g]);
+            vb_[kk] = *reinterpret_cast<const u32x4*>(&s.v[16 * w + r][32 * kk + 8 * g]);
+        }
+        __syncthreads();   // every wave is done with the K / V tiles
+        // each wave publishes its 16 query rows of Q and dO, LSE and delta
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) {
+            *reinterpret_cast<u32x4*>(&su.x.q[16 * w + r][32 * kk + 8 * g]) = qb[kk];
+            *reinterpret_cast<u32x4*>(&su.x.d_o[16 * w + r][32 * kk + 8 * g]) = db[kk];
+        }
+        if (g == 0) {
+            su.x.lse2[16 * w + r] = lse2;
+            su.x.delta[16 * w + r] = qv ? delta : 0.0f;
+        }
+        __syncthreads();
+        u32x2 pb[kRows / 16], dsq[kRows / 16];
+#pragma unroll
+        for (int qb_ = 0; qb_ < kRows / 16; ++qb_) {
+            // S = Q K^T and dP = dO V^T: lane holds [query 16 qb_ + 4 g + i][key r]
+            f32x4 st = {0.f, 0.f, 0.f, 0.f}, dpt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk) {
+                st = mfma32(*reinterpret_cast<const u32x4*>(&su.x.q[16 * qb_ + r][32 * kk + 8 * g]), kb_[kk], st);
+                dpt = mfma32(*reinterpret_cast<const u32x4*>(&su.x.d_o[16 * qb_ + r][32 * kk + 8 * g]), vb_[kk], dpt);
+            }
+            float pr[4], dsr[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int qi = 16 * qb_ + 4 * g + i;
+                pr[i] = exp2_hw(st[i] * sc - su.x.lse2[qi]);
+                dsr[i] = pr[i] * (dpt[i] - su.x.delta[qi]);
+            }
+            pb[qb_] = u32x2{pack_bf16(pr[0], pr[1]), pack_bf16(pr[2], pr[3])};
+            dsq[qb_] = u32x2{pack_bf16(dsr[0], dsr[1]), pack_bf16(dsr[2], dsr[3])};
+        }
+        // dV^T = dO^T P, then dK^T = Q^T dS, over two 32-query halves (one
+        // accumulator set live at a time keeps the register count of the
+        // streaming loop)
+        const int j = key0 + 16 * w + r;   // trainable key index
+        const size_t row = (bh * (size_t)bound + j) * D;
+#pragma unroll 1
+        for (int which = 0; which < 2; ++which) {
+            const u32x2* op = which == 0 ? pb : dsq;
+            f32x4 c[D / 16];
+#pragma unroll
+            for (int nb = 0; nb < D / 16; ++nb) c[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int h = 0; h < kRows / 32; ++h) {
+                const u32x4 bop = {op[2 * h].x, op[2 * h].y, op[2 * h + 1].x, op[2 * h + 1].y};
+#pragma unroll
+                for (int nb = 0; nb < D / 16; ++nb) {
+                    const int k0 = 32 * h + 4 * g, k1 = 32 * h + 16 + 4 * g;
+                    const u32x4 aop = which == 0 ? tr_pair(su.x.d_o, k0, k1, 16 * nb, r)
+                                                 : tr_pair(su.x.q, k0, k1, 16 * nb, r);
+                    c[nb] = mfma32(aop, bop, c[nb]);
+                }
+            }
+            if (j < bound) {
+                float* out = (which == 0 ? a.dv : a.dk) + row;
+                const float f = which == 0 ? 1.0f : a.scale;
+#pragma unroll
+                for (int nb = 0; nb < D / 16; ++nb) *reinterpret_cast<f32x4*>(out + 16 * nb + 4 * g) = c[nb] * f;
+            }
+        }
+    };
     auto tile = [&](int t) {
         const int key0 = kt.row_of(t), bound = kt.bound_of(t);
         u32x2 dsb[kRows / 16];
@@ -368,6 +463,9 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq(AttnArgs a) {
 #pragma unroll
             for (int nb = 0; nb < D / 16; ++nb)
                 acc[nb] = mfma32(tr_pair(s.kr, 32 * h + 4 * g, 32 * h + 16 + 4 * g, 16 * nb, r), bop, acc[nb]);
+        }
+        if constexpr (FUSE_KV) {
+            if (t < kt.n && kt.src_of(t) == 1) tile_dkdv(key0, bound);
         }
     };
     // K is loaded once and written twice, at the pitch of each way it is read.
@@ -503,10 +601,16 @@ hipError_t launch_fwd(const AttnArgs& a, hipStream_t st) {
 template <int D>
 hipError_t launch_bwd(const AttnArgs& a, hipStream_t st) {
     dim3 grid_q((a.lq + kRows - 1) / kRows, a.heads, a.batch);
-    hipLaunchKernelGGL(attn_bwd_dq<D>, grid_q, dim3(kThreads), 0, st, a);
+    const int lt = a.src[1].rows;
+    if (a.lq <= kRows && lt > 0) {
+        // one workgroup holds every query of its (batch, head): dK and dV
+        // come out of the same kernel
+        hipLaunchKernelGGL((attn_bwd_dq<D, true>), grid_q, dim3(kThreads), 0, st, a);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((attn_bwd_dq<D, false>), grid_q, dim3(kThreads), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int lt = a.src[1].rows;
     if (lt > 0) {
         dim3 grid_k((lt + kRows - 1) / kRows, a.heads, a.batch);
         hipLaunchKernelGGL(attn_bwd_dkdv<D>, grid_k, dim3(kThreads), 0, st, a);
