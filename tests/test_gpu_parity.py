@@ -530,6 +530,64 @@ def test_working_copy_odd_vector_counts(shift):
     opt.close()
 
 
+def test_two_handles_on_two_streams_from_two_threads():
+    """Handles share no state: two tables, each on its own stream, stepped
+    from two host threads at once (the ABI asks only that one handle is used
+    by one thread at a time), each matching its own oracle."""
+    import threading
+    wls = [W.tiny(seed_offset=11, n_tensors=12, max_numel=20000),
+           W.tiny(seed_offset=12, n_tensors=9, max_numel=30000)]
+    runs = []
+    for wl in wls:
+        st = allocate(wl)
+        p0 = [host(x) for x in st.p]
+        stream = torch.cuda.Stream()
+        opt = make_handle(wl, st, stream=stream)
+        opt.capture()
+        runs.append((wl, st, opt, make_oracle(wl, p0), stream))
+    # gradients of all three steps are drawn up front on the default stream
+    grads = []
+    for wl, st, _, _, _ in runs:
+        per_step = []
+        for k in range(1, 4):
+            fill_grads(wl, st, k)
+            per_step.append([g.clone() for g in st.g])
+        grads.append(per_step)
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(idx):
+        try:
+            wl, st, opt, _, stream = runs[idx]
+            with torch.cuda.stream(stream):
+                for k in range(3):
+                    for dst, src in zip(st.g, grads[idx][k]):
+                        dst.copy_(src)
+                    opt.replay(stream)
+            stream.synchronize()
+        except Exception as e:      # reported on the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for idx, (wl, st, opt, ora, _) in enumerate(runs):
+        for k in range(3):
+            ora.step([host(g) for g in grads[idx][k]])
+        for i, t in enumerate(wl.tensors):
+            if t.trainable:
+                assert_close(f"h{idx} p[{i}]", host(st.p[i]), ora.p[i])
+                assert_close(f"h{idx} m[{i}]", host(st.m[i]), ora.m[i])
+                assert_close(f"h{idx} v[{i}]", host(st.v[i]), ora.v[i])
+        _, steps = opt.read_stats()
+        assert steps == [3] * len(wl.groups)
+        opt.close()
+
+
 def test_setters_mid_run_and_side_stream():
     """Change max_norm / divisor and the hyperparameters between steps, reset
     the step count on a live handle, and run everything on a non-default
