@@ -169,7 +169,9 @@ typedef struct somaopt_handle somaopt_handle;
  * maximum elements per workgroup of the norm / update pass (the update pass
  * at most 2^26); SOMAOPT_PASS1_WG_PER_CU, SOMAOPT_PASS2_WG_PER_CU = resident
  * workgroups per compute unit (0: no limit; unset: chosen from the table
- * shape, reported in somaopt_plan_info).
+ * shape, reported in somaopt_plan_info); SOMAOPT_SEGMENT_COST,
+ * SOMAOPT_UPDATE_SEGMENT_COST = elements charged per segment when short
+ * segments are packed into the norm / update pass's workgroups (1024, 4096).
  */
 int somaopt_init_tensor_table(const somaopt_tensor_desc* descs, int64_t n_tensors,
                               const somaopt_group* groups, int32_t n_groups,

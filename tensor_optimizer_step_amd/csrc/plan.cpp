@@ -240,6 +240,7 @@ Plan build_plan(const somaopt_tensor_desc* d, int64_t n, int pass, int64_t chunk
         }
     }
     // Pack consecutive segments into workgroups of bounded cost.
+    if (segment_cost < 0) segment_cost = default_segment_cost(pass);
     plan.block_first.clear();
     int64_t cost = 0;
     for (size_t s = 0; s < plan.segs.size(); ++s) {

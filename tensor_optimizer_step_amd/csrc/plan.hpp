@@ -62,9 +62,16 @@ static_assert(sizeof(Seg2) == 64, "Seg2 layout");
 constexpr int64_t kDefaultPass1Chunk = 8192;
 constexpr int64_t kDefaultPass2Chunk = 4096;
 // Packing cost of one segment, in elements: a segment costs about one memory
-// latency before its loads are in flight.  Measured on the 20,000-tensor
-// workload: 1024 beats 64 by 3% per step; large tensors are unaffected.
+// latency before its loads are in flight.  Measured on MI355X: for the norm
+// (and arrival) pass 1024 beats 64 by 3% per step on the 20,000-tensor
+// workload; for the update pass 4096, which keeps about one segment per
+// workgroup, beats 1024 by 4% there and halves the 64-tensor workload's
+// update pass (more workgroups each wait on one segment instead of a few
+// walking several in turn).  Tables of full-length segments are unaffected.
 constexpr int64_t kSegmentCost = 1024;
+constexpr int64_t kUpdateSegmentCost = 4096;
+// Packing cost used by build_plan for `pass` when the caller gives none.
+inline int64_t default_segment_cost(int pass) { return pass == 2 ? kUpdateSegmentCost : kSegmentCost; }
 
 struct PlanSeg {
     int64_t tensor;
@@ -102,8 +109,9 @@ int validate_arrival(const somaopt_tensor_desc* d, int64_t n, const void* const*
 
 // pass = 1 (owned gradient segments), 2 (all trainable segments, aligned for
 // p/m/v/g) or 3 (all trainable segments, aligned for g and incoming[i]).
+// segment_cost < 0: default_segment_cost(pass).
 Plan build_plan(const somaopt_tensor_desc* d, int64_t n, int pass, int64_t chunk,
-                int64_t segment_cost = kSegmentCost, const void* const* incoming = nullptr);
+                int64_t segment_cost = -1, const void* const* incoming = nullptr);
 
 // Largest update-pass segment: its vector body is addressed with 32-bit byte
 // offsets (16 bytes per 4-element vector) by the buffer instructions.

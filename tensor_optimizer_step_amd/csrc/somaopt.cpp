@@ -303,9 +303,10 @@ int somaopt_init_tensor_table(const somaopt_tensor_desc* descs, int64_t n_tensor
 
     const int64_t ch1 = normalise_chunk(env_int("SOMAOPT_PASS1_CHUNK", 0), kDefaultPass1Chunk);
     const int64_t ch2 = normalise_chunk(env_int("SOMAOPT_PASS2_CHUNK", 0), kDefaultPass2Chunk, kMaxPass2Chunk);
-    const int64_t seg_cost = std::max<int64_t>(0, env_int("SOMAOPT_SEGMENT_COST", kSegmentCost));
-    Plan p1 = build_plan(descs, n_tensors, 1, ch1, seg_cost);
-    Plan p2 = build_plan(descs, n_tensors, 2, ch2, seg_cost);
+    const int64_t cost1 = std::max<int64_t>(0, env_int("SOMAOPT_SEGMENT_COST", kSegmentCost));
+    const int64_t cost2 = std::max<int64_t>(0, env_int("SOMAOPT_UPDATE_SEGMENT_COST", kUpdateSegmentCost));
+    Plan p1 = build_plan(descs, n_tensors, 1, ch1, cost1);
+    Plan p2 = build_plan(descs, n_tensors, 2, ch2, cost2);
     if (p1.segs.size() >= 0xFFFFFFFFull || p2.segs.size() >= 0xFFFFFFFFull)
         return fail(SOMAOPT_E_INVALID, "too many segments for 32-bit indices");
     // A dispatch holds fewer than 2^32 work-items.

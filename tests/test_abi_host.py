@@ -157,9 +157,21 @@ def test_plan_frozen_and_not_owned():
 def test_plan_many_small_tensors_pack_into_few_blocks():
     sizes = list(np.random.default_rng(1).integers(1, 4097, size=2000))
     rows = _rows(sizes)
+    # norm pass: 1,024 elements charged per segment, budget chunk + 1,024
+    segs, info = S.debug_plan(rows, 1, 1, 8192, 0)
+    assert info.pass1_blocks < len(sizes) / 2
+    assert info.pass1_segments == len(sizes)
+    # update pass: 4,096 charged per segment -- small tensors pack in pairs at most
+    # under a chunk of 8,192, and one per workgroup under the default 4,096
     segs, info = S.debug_plan(rows, 1, 2, 0, 8192)
-    assert info.pass2_blocks < len(sizes) / 2
+    assert len(sizes) / 3 < info.pass2_blocks < len(sizes)
     assert info.pass2_segments == len(sizes)
+    blocks = {}
+    for sg in segs:
+        blocks[sg.block] = blocks.get(sg.block, 0) + sg.numel + 4096
+    assert max(blocks.values()) <= 8192 + 4096
+    segs, info = S.debug_plan(rows, 1, 2, 0, 0)
+    assert info.pass2_blocks == len(sizes)
 
 
 def test_occupancy_follows_the_table_shape():
