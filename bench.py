@@ -533,6 +533,18 @@ def main():
     print(f"[bench] {args.steps} graph steps: {step_s * 1e3:.4f} ms/step", file=sys.stderr,
           flush=True)
 
+    # the same K steps launched eagerly (two calls per step, no graph), for context
+    e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e_a.record(stream)
+    for k in range(args.steps):
+        if host_sched:
+            opt.set_lrs(wl.lrs_for_step(1 + k % wl.steps), stream)
+        opt.step(stream)
+    e_b.record(stream)
+    torch.cuda.synchronize()
+    eager_ms = e_a.elapsed_time(e_b) / args.steps
+
     # per-kernel durations: eager steps with HIP events on the launch stream
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
@@ -571,6 +583,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": step_s * 1e3,
+        "eager_ms_per_step": round(eager_ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
