@@ -639,7 +639,7 @@ int somaopt_capture_arrival_step(somaopt_handle* h, int32_t accumulate) {
 int somaopt_replay_step(somaopt_handle* h, void* stream) {
     if (!h) return fail(SOMAOPT_E_INVALID, "handle is NULL");
     if (!h->exec) return fail(SOMAOPT_E_STATE, "no captured step (call somaopt_capture_step)");
-    if (h->pending) return fail(SOMAOPT_E_STATE, "an eager norm pass is pending; finish it with somaopt_fused_adamw_step");
+    if (h->pending) return fail(SOMAOPT_E_STATE, "an eager norm or arrival pass is pending; finish it with somaopt_fused_adamw_step");
     DeviceGuard g(h->device);
     if (!g.ok()) return fail(SOMAOPT_E_HIP, "cannot select the handle's device");
     hipError_t e = hipGraphLaunch(h->exec, static_cast<hipStream_t>(stream));

@@ -136,6 +136,8 @@ def test_arrival_call_order_and_validation():
     lib = somaopt.load()
     with pytest.raises(somaopt.SomaoptError, match="register_arrival must precede"):
         opt.arrival_sqnorm(True)
+    with pytest.raises(somaopt.SomaoptError, match="register_arrival must precede"):
+        opt.capture_arrival(True)
     inc = _incoming(wl, st, False)
     with pytest.raises(somaopt.SomaoptError, match="n_tensors differs"):
         opt.register_arrival(inc[:-1])
@@ -152,8 +154,17 @@ def test_arrival_call_order_and_validation():
         opt.register_arrival(inc)
     with pytest.raises(somaopt.SomaoptError, match="accumulate"):
         somaopt._check(lib.somaopt_arrival_sqnorm(opt._h, 2, None))
+    with pytest.raises(somaopt.SomaoptError, match="accumulate"):
+        somaopt._check(lib.somaopt_capture_arrival_step(opt._h, -1))
     opt.arrival_sqnorm(False)
     opt.fused_adamw_step()
+    # a replay is a whole step: refused while an eager pass is pending
+    opt.capture_arrival(False)
+    opt.arrival_sqnorm(False)
+    with pytest.raises(somaopt.SomaoptError, match="pending"):
+        opt.replay()
+    opt.fused_adamw_step()
+    opt.replay()
     torch.cuda.synchronize()
     opt.close()
 
