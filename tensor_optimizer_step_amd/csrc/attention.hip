@@ -171,6 +171,37 @@ __device__ __forceinline__ void two_stage_tiles(int n_tiles, Stage& s0, Stage& s
     }
 }
 
+// Workgroup coordinates (query block, head, batch) grouped by XCD.  The
+// hardware hands consecutive workgroups to the eight XCDs in turn, each with
+// its own L2; this bijection gives every XCD one contiguous run of the
+// logical order, in which the query batches that share one context batch
+// (ctx_share of them, same head) are adjacent -- so a shared context is read
+// from HBM into one XCD's L2 and reused there (measured on MI355X, 64 query
+// batches sharing contexts by 2 over 12 heads: forward 71.6 -> 61.3 us; by 4
+// over 6 heads: 42.9 -> 40.1 us).  Without sharing the plain order is kept.
+// Only placement depends on the dispatch order; any order computes the same
+// result.
+struct WgCoord {
+    int x, h, b;
+};
+__device__ __forceinline__ WgCoord xcd_grouped(int share) {
+    if (share <= 1) return WgCoord{(int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z};
+    const uint32_t nx = gridDim.x, nh = gridDim.y, nb = gridDim.z;
+    const uint32_t n = nx * nh * nb;
+    const uint32_t l = blockIdx.x + nx * (blockIdx.y + nh * blockIdx.z);
+    const uint32_t xcd = l % 8, local = l / 8, per = n / 8, rem = n % 8;
+    uint32_t t = xcd * per + (xcd < rem ? xcd : rem) + local;   // logical index
+    WgCoord c;
+    c.x = (int)(t % nx);
+    t /= nx;
+    const uint32_t sh = (uint32_t)share;
+    const uint32_t m = t % sh;
+    t /= sh;
+    c.h = (int)(t % nh);
+    c.b = (int)((t / nh) * sh + m);
+    return c;
+}
+
 // The key tiles of one (batch, head): the tiles of the frozen source, then
 // those of the trainable source.  Resources are built once; picking one per
 // tile is a uniform (scalar) choice.
@@ -210,10 +241,11 @@ __global__ __launch_bounds__(kThreads) void attn_fwd(AttnArgs a) {
     __shared__ FwdLds<D> s;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
-    const size_t bh = (size_t)blockIdx.z * a.heads + blockIdx.y;
+    const WgCoord wc = xcd_grouped(a.src[0].share);
+    const size_t bh = (size_t)wc.b * a.heads + wc.h;
     const auto Q = mat_rsrc<D>(static_cast<const uint16_t*>(a.q) + bh * a.lq * D, a.lq);
-    const KeyTiles<D> kt(a, blockIdx.z, blockIdx.y);
-    const int q = blockIdx.x * kRows + 16 * w + r;
+    const KeyTiles<D> kt(a, wc.b, wc.h);
+    const int q = wc.x * kRows + 16 * w + r;
     const bool qv = q < a.lq;
     // B operand of S^T = K Q^T: Q[q][32 kk + 8 g .. + 7] (zero past the last query)
     u32x4 qb[D / 32];
@@ -339,12 +371,13 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq(AttnArgs a) {
     DqLds<D>& s = su.t;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
-    const size_t bh = (size_t)blockIdx.z * a.heads + blockIdx.y;
+    const WgCoord wc = xcd_grouped(a.src[0].share);
+    const size_t bh = (size_t)wc.b * a.heads + wc.h;
     const auto Q = mat_rsrc<D>(static_cast<const uint16_t*>(a.q) + bh * a.lq * D, a.lq);
     const auto dO = mat_rsrc<D>(static_cast<const uint16_t*>(a.d_o) + bh * a.lq * D, a.lq);
     const auto O = mat_rsrc<D>(static_cast<const uint16_t*>(a.o) + bh * a.lq * D, a.lq);
-    const KeyTiles<D> kt(a, blockIdx.z, blockIdx.y);
-    const int q = blockIdx.x * kRows + 16 * w + r;
+    const KeyTiles<D> kt(a, wc.b, wc.h);
+    const int q = wc.x * kRows + 16 * w + r;
     const bool qv = q < a.lq;
     u32x4 qb[D / 32], db[D / 32];
     float dot = 0.0f;

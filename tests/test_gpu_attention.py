@@ -130,6 +130,8 @@ CTX_CASES = [
     (2, 2, 33, 0, 70, 1, 128),
     (4, 1, 17, 65, 1, 2, 64),
     (2, 2, 130, 7, 129, 1, 128),
+    (10, 3, 20, 70, 9, 5, 64),     # 30 workgroups: the XCD grouping's uneven remainder
+    (8, 5, 96, 64, 0, 4, 64),      # two query blocks per (batch, head), shared context, no action keys
 ]
 
 
