@@ -202,15 +202,19 @@ __device__ __forceinline__ WgCoord xcd_grouped(int share) {
     return c;
 }
 
-// The key tiles of one (batch, head): the tiles of the frozen source, then
-// those of the trainable source.  Resources are built once; picking one per
-// tile is a uniform (scalar) choice.
+// The key tiles of one (batch, head), source by source.  Resources are built
+// once; picking one per tile is a uniform (scalar) choice.
 template <int D>
+//
+// The frozen source comes first, or, with trainable_first, the trainable
+// one: the dQ kernel that also produces dK/dV visits the trainable tiles
+// first, so their extra products overlap the loads of the frozen tiles
+// instead of trailing after the last load.
 struct KeyTiles {
     __amdgpu_buffer_rsrc_t k[2], v[2];
     int rows[2];
-    int n0, n;   // tiles of source 0, tiles in total
-    __device__ __forceinline__ KeyTiles(const AttnArgs& a, int b, int h) {
+    int first, nf, n;   // source visited first, its tile count, tiles in total
+    __device__ __forceinline__ KeyTiles(const AttnArgs& a, int b, int h, bool trainable_first = false) {
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const KeySrc& src = a.src[s];
@@ -219,13 +223,15 @@ struct KeyTiles {
             v[s] = mat_rsrc<D>(static_cast<const uint16_t*>(src.v) + off, src.rows);
             rows[s] = src.rows;
         }
-        n0 = (rows[0] + kRows - 1) / kRows;
-        n = n0 + (rows[1] + kRows - 1) / kRows;
+        first = trainable_first ? 1 : 0;
+        nf = (rows[first] + kRows - 1) / kRows;
+        n = nf + (rows[1 - first] + kRows - 1) / kRows;
     }
-    // Source and first row of tile t (tiles past the end fall past source 1).
-    __device__ __forceinline__ int src_of(int t) const { return t < n0 ? 0 : 1; }
-    __device__ __forceinline__ int row_of(int t) const { return (t < n0 ? t : t - n0) * kRows; }
-    __device__ __forceinline__ int bound_of(int t) const { return t < n0 ? rows[0] : rows[1]; }
+    // Source and first row of tile t (tiles past the end fall past the end
+    // of the source visited second).
+    __device__ __forceinline__ int src_of(int t) const { return t < nf ? first : 1 - first; }
+    __device__ __forceinline__ int row_of(int t) const { return (t < nf ? t : t - nf) * kRows; }
+    __device__ __forceinline__ int bound_of(int t) const { return rows[src_of(t)]; }
 };
 
 // ------------------------------------------------------------------ forward
@@ -376,7 +382,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dq(AttnArgs a) {
     const auto Q = mat_rsrc<D>(static_cast<const uint16_t*>(a.q) + bh * a.lq * D, a.lq);
     const auto dO = mat_rsrc<D>(static_cast<const uint16_t*>(a.d_o) + bh * a.lq * D, a.lq);
     const auto O = mat_rsrc<D>(static_cast<const uint16_t*>(a.o) + bh * a.lq * D, a.lq);
-    const KeyTiles<D> kt(a, wc.b, wc.h);
+    const KeyTiles<D> kt(a, wc.b, wc.h, FUSE_KV);
     const int q = wc.x * kRows + 16 * w + r;
     const bool qv = q < a.lq;
     u32x4 qb[D / 32], db[D / 32];
