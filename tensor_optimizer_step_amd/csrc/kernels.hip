@@ -235,8 +235,8 @@ __device__ __forceinline__ double int_pow(double b, int64_t t) {
 // those of somaopt_set_schedules.
 __device__ double scheduled_lr(const somaopt_schedule& s, int64_t t, double lr) {
     if (s.kind == SOMAOPT_SCHED_NONE) return lr;
-    const int64_t w = s.kind == SOMAOPT_SCHED_COSINE ? 0 : s.warmup;
-    if (s.kind == SOMAOPT_SCHED_LINEAR_WARMUP || t <= w) {
+    const int64_t w = s.kind == SOMAOPT_SCHED_COSINE ? 0 : s.warmup;   // >= 1 for the warm-up kinds
+    if (s.kind == SOMAOPT_SCHED_LINEAR_WARMUP || (w > 0 && t <= w)) {
         const int64_t tt = t < w ? (t < 0 ? 0 : t) : w;
         return s.peak_lr * (double)tt / (double)w;
     }
