@@ -220,6 +220,76 @@ def device_schedules(somaopt, wl):
     raise ValueError(f"no device form for schedule {wl.schedule!r}")
 
 
+def cpu_baseline_arrival(wl, seconds: float, accumulate: bool) -> dict:
+    """The fp64 oracles of the arrival step (accumulate or copy, then the clip +
+    AdamW step) on the first tensors of the workload (bounded)."""
+    import oracle as O
+    from tensor_optimizer_step_amd import workloads as W
+
+    budget = 20_000_000
+    idx, tot = [], 0
+    for i, t in enumerate(wl.tensors):
+        if not t.trainable:
+            continue
+        if idx and tot + t.numel > budget:
+            break
+        idx.append(i)
+        tot += t.numel
+    p0 = [W.param_values(wl, i).numpy() for i in idx]
+    held = [W.to_numpy_grad(W.grad_values(wl, i, 1)) for i in idx]
+    inc = [W.to_numpy_grad(W.grad_values(wl, i, 2)) for i in idx]
+    ora = O.Oracle(p0, [True] * len(idx), [True] * len(idx), [wl.tensors[i].group for i in idx],
+                   [O.Group(h.lr, h.weight_decay, h.beta1, h.beta2, h.eps) for h in wl.groups],
+                   wl.max_norm, wl.grad_divisor)
+
+    def step():
+        new = [O.accumulate_gradient(hg, ig, accumulate) for hg, ig in zip(held, inc)]
+        ora.step(new)
+
+    step()                             # untimed warm-up (page faults)
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < 3 or time.perf_counter() - t_start < seconds:
+        t0 = time.perf_counter()
+        step()
+        times.append(time.perf_counter() - t0)
+    med = sorted(times)[len(times) // 2]
+    return {"value": tot / med, "unit": "param-elements/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {len(idx)} tensors of {wl.name} ({tot} elements), "
+                      f"{len(times)} timed steps, median step {med:.3f} s, NumPy float64, one thread"}
+
+
+def cpu_baseline_attention(torch, shape: dict, seconds: float) -> dict:
+    """The fp64 attention oracle (forward, then backward with the frozen
+    context) on a few (batch, head) pairs of the bench shape, scaled to the
+    whole batch; BLAS limited to one thread."""
+    import numpy as np
+    import oracle as O
+    from threadpoolctl import threadpool_limits
+
+    b, h, lq, lc, la, d = (shape[k] for k in ("batch", "heads", "lq", "l_ctx", "l_act", "head_dim"))
+    lk = lc + la
+    g = torch.Generator()
+    g.manual_seed(4100)
+    mk = lambda *x: torch.randn(*x, generator=g).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    pairs = 4
+    q, k, v, do = mk(pairs, lq, d), mk(pairs, lk, d), mk(pairs, lk, d), mk(pairs, lq, d)
+    scale = 1.0 / np.sqrt(d)
+    times = []
+    with threadpool_limits(limits=1):
+        O.attention_forward(q, k, v, scale)          # untimed warm-up
+        t_start = time.perf_counter()
+        while len(times) < 3 or time.perf_counter() - t_start < seconds:
+            t0 = time.perf_counter()
+            o, lse = O.attention_forward(q, k, v, scale)
+            O.attention_backward(q, k, v, o, lse, do, scale, lc)
+            times.append(time.perf_counter() - t0)
+    med = sorted(times)[len(times) // 2]
+    return {"value": med / pairs * b * h * 1e6, "unit": "us per forward+backward", "cores": 1, "kind": "oracle",
+            "sample": f"{pairs} of the {b * h} (batch, head) pairs, {len(times)} timed runs, median "
+                      f"{med:.3f} s, scaled by {b * h}/{pairs}; NumPy float64, BLAS on one thread"}
+
+
 def plain_setup(torch, somaopt, W, wl, dev, stream, lowp_dtype):
     """One allocation per tensor: seeded fp32 weights, zero moments, step-1 grads."""
     print(f"[bench] {wl.name}: {wl.n_tensors} tensors, {wl.trainable_numel} trainable elements",
@@ -408,6 +478,7 @@ def attention_bench(torch, args):
         "roofline": {"bound": "hbm", "achieved": round(bytes_f / ms_f / 1e6, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(bytes_f / ms_f / 1e6 / HBM_PEAK_GBS, 4), "traffic": None,
                      "kernel": "attn_fwd"},
+        "cpu_baseline": (cpu_baseline_attention(torch, sh, args.cpu_seconds) if args.cpu_seconds > 0 else None),
         "wall_s": wall,
     }
     print(json.dumps(out), flush=True)
@@ -458,6 +529,18 @@ def arrival_bench(torch, args, wl, opt, keep, stream, bts):
     e1.record(stream)
     torch.cuda.synchronize()
     ms_fused = e0.elapsed_time(e1) / args.steps
+    # per-call durations on the launch stream: arrival (+ its reduction) and update
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for a0, a1, a2 in ev:
+        a0.record(stream)
+        opt.arrival_sqnorm(acc, stream)
+        a1.record(stream)
+        opt.fused_adamw_step(stream)
+        a2.record(stream)
+    torch.cuda.synchronize()
+    arr_ms = sum(x.elapsed_time(y) for x, y, _ in ev) / len(ev)
+    upd_ms = sum(y.elapsed_time(z) for _, y, z in ev) / len(ev)
     stats, _ = opt.read_stats()
     if not all(math.isfinite(x) for x in (stats.norm, stats.clip_coef)):
         raise RuntimeError("non-finite statistics in the benchmark run")
@@ -477,6 +560,13 @@ def arrival_bench(torch, args, wl, opt, keep, stream, bts):
         "separate_norm_pass": {"ms_per_step": ms_sep, "model_bytes_per_step": sep_bytes,
                                "hbm_GBps": round(sep_bytes / ms_sep / 1e6, 1), "launches": "eager"},
         "saved_ms_per_step": ms_sep - ms_eager,
+        "roofline": {"bound": "hbm", "kernel": "adamw_pass2",
+                     "achieved": round(bts["pass2"] / (upd_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(bts["pass2"] / (upd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": None, "avg_launch_ms": round(upd_ms, 5),
+                     "arrival_call_avg_ms": round(arr_ms, 5),
+                     "arrival_call_GBps": round(arrival_bytes / (arr_ms * 1e-3) / 1e9, 1)},
+        "cpu_baseline": (cpu_baseline_arrival(wl, args.cpu_seconds, acc) if args.cpu_seconds > 0 else None),
     }
     opt.close()
     print(json.dumps(out), flush=True)
