@@ -9,7 +9,7 @@
  *      once,
  *   3. take one global clip decision  c = min(1, max_norm / (norm + 1e-6))
  *      (the clip_grad_norm_ rule the veRL page applies with max_norm = 1.0,
- *      section 4.2 "Phase 4: Actor Update"),
+ *      "Phase 4: Actor Update", section 4.2 "PPO Update"),
  *   4. in one fused pass that reads the ORIGINAL gradient, apply
  *      normalization, clipping and decoupled-weight-decay AdamW to the fp32
  *      weight and both fp32 moments, per parameter group:

@@ -14,7 +14,8 @@ title; they name the post-backward work and its fused form):
    owned element counts once (every gradient shard enters exactly once);
 3. take one global clipping decision c = min(1, max_norm / (norm + 1e-6)),
    the torch ``clip_grad_norm_`` rule the veRL page calls with max_norm=1.0
-   (section 4.2, "Gradient Clipping and Optimizer Step");
+   ("Phase 4: Actor Update", section 4.2 "PPO Update": the gradient clip and
+   optimizer step that follow the accumulated micro-batches);
 4. update weights and both running moments with decoupled-weight-decay AdamW
    from the original gradients, per parameter group, with fp32 states widened
    to fp64 (RLinf page, "Retaining Low-Precision Gradients": gradients are
