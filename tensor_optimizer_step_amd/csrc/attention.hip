@@ -4,10 +4,12 @@
 // SomaSpeed landing page, paragraph 5: queries from the trainable action
 // computation read the context keys/values tile by tile, the full score
 // matrix is never stored, and frozen inputs get no gradient work.  Here the
-// first lk_frozen keys of every (batch, head) are frozen: the backward produces
-// dQ for every query and dK/dV only for the trainable keys -- the frozen
-// tiles cost three products per tile (S, dP, dQ) instead of five, and the
-// dK/dV kernel is never launched over them.
+// keys of every (batch, head) are a frozen source followed by a trainable one:
+// the backward produces dQ for every query and dK/dV only for the trainable
+// keys -- the frozen tiles cost three products per tile (S, dP, dQ) instead of
+// five.  dK/dV come out of the dQ kernel itself when one workgroup holds all
+// queries of a (batch, head) (at most 64), else from a second kernel launched
+// over the trainable keys only.
 //
 // Layout: Q, K, V, O, dO are bf16 [B][H][L][D], rows contiguous; LSE and
 // delta fp32 [B][H][Lq]; dQ fp32 [B][H][Lq][D]; dK, dV fp32 [B][H][Lk-Lf][D].
