@@ -178,16 +178,18 @@ __device__ __forceinline__ void two_stage_tiles(int n_tiles, Stage& s0, Stage& s
 // its own L2; this bijection gives every XCD one contiguous run of the
 // logical order, in which the query batches that share one context batch
 // (ctx_share of them, same head) are adjacent -- so a shared context is read
-// from HBM into one XCD's L2 and reused there (measured on MI355X, 64 query
-// batches sharing contexts by 2 over 12 heads: forward 71.6 -> 61.3 us; by 4
-// over 6 heads: 42.9 -> 40.1 us).  Without sharing the plain order is kept.
-// Only placement depends on the dispatch order; any order computes the same
-// result.
+// from HBM into one XCD's L2 and reused there; so are the query blocks of
+// one (batch, head), which read the same keys (measured on MI355X, 64 query
+// batches, 960 context keys: contexts shared by 2 over 12 heads 71.6 -> 61.3
+// us; 128 queries per head 90.2 -> 79.8 us, 256 queries 165 -> 130 us).  With
+// one query block and no sharing nothing is reused and the plain order is
+// kept.  Only placement depends on the dispatch order; any order computes the
+// same result.
 struct WgCoord {
     int x, h, b;
 };
 __device__ __forceinline__ WgCoord xcd_grouped(int share) {
-    if (share <= 1) return WgCoord{(int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z};
+    if (share <= 1 && gridDim.x == 1) return WgCoord{(int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z};
     const uint32_t nx = gridDim.x, nh = gridDim.y, nb = gridDim.z;
     const uint32_t n = nx * nh * nb;
     const uint32_t l = blockIdx.x + nx * (blockIdx.y + nh * blockIdx.z);
@@ -549,15 +551,16 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_dkdv(AttnArgs a) {
     __shared__ DkvLds<D> s;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
-    const size_t bh = (size_t)blockIdx.z * a.heads + blockIdx.y;
+    const WgCoord wc = xcd_grouped(1);   // key blocks of one (batch, head) share its Q and dO
+    const size_t bh = (size_t)wc.b * a.heads + wc.h;
     const KeySrc& src = a.src[1];
     const int lt = src.rows;
     const auto Q = mat_rsrc<D>(static_cast<const uint16_t*>(a.q) + bh * a.lq * D, a.lq);
     const auto dO = mat_rsrc<D>(static_cast<const uint16_t*>(a.d_o) + bh * a.lq * D, a.lq);
-    const size_t koff = ((size_t)(blockIdx.z / src.share) * a.heads + blockIdx.y) * (size_t)src.stride * D;
+    const size_t koff = ((size_t)(wc.b / src.share) * a.heads + wc.h) * (size_t)src.stride * D;
     const auto K = mat_rsrc<D>(static_cast<const uint16_t*>(src.k) + koff, lt);
     const auto V = mat_rsrc<D>(static_cast<const uint16_t*>(src.v) + koff, lt);
-    const int j = blockIdx.x * kRows + 16 * w + r;   // trainable key index
+    const int j = wc.x * kRows + 16 * w + r;   // trainable key index
     const bool kv = j < lt;
     const int key = j;
     // B operands: K[key][32 kk + 8 g ..], V[key][32 kk + 8 g ..] (zero past the last key)
