@@ -137,16 +137,30 @@ CTX_CASES = [
 
 @pytest.mark.parametrize("case", CTX_CASES, ids=lambda c: "b{}h{}q{}c{}a{}s{}d{}".format(*c))
 def test_attention_context_and_action_buffers(case):
+    _run_ctx_case(case)
+
+
+@pytest.mark.parametrize("case", [(4, 2, 50, 130, 40, 2, 128), (2, 2, 96, 70, 64, 1, 64)],
+                         ids=lambda c: "b{}h{}q{}c{}a{}s{}d{}".format(*c))
+def test_attention_peaked_scores(case):
+    """Queries and keys four times larger: scores with a standard deviation of
+    about 16, so most weights of a row underflow and one or two keys dominate
+    (fused dK/dV path and the separate one)."""
+    _run_ctx_case(case, amp=4.0)
+
+
+def _run_ctx_case(case, amp=1.0):
     from tensor_optimizer_step_amd import somaopt
     b, h, lq, lc, la, share, d = case
-    log(f"[attention ctx] case {case}")
+    log(f"[attention ctx] case {case} amplitude {amp}")
     g = torch.Generator(device="cuda")
     g.manual_seed(1000 + sum(case))
     mk = lambda *s: torch.randn(*s, generator=g, device="cuda").to(torch.bfloat16)
-    q, do = mk(b, h, lq, d), mk(b, h, lq, d)
-    kc = mk(b // share, h, lc, d) if lc else None
+    mka = lambda *s: (torch.randn(*s, generator=g, device="cuda") * amp).to(torch.bfloat16)
+    q, do = mka(b, h, lq, d), mk(b, h, lq, d)
+    kc = mka(b // share, h, lc, d) if lc else None
     vc = mk(b // share, h, lc, d) if lc else None
-    ka = mk(b, h, la, d) if la else None
+    ka = mka(b, h, la, d) if la else None
     va = mk(b, h, la, d) if la else None
     scale = 1.0 / math.sqrt(d)
     o = torch.empty_like(q)
