@@ -1,0 +1,130 @@
+"""Randomized tables through the C-ABI against the fp64 oracle.
+
+Each seed draws a table that mixes what the targeted tests cover one at a
+time: fp32, bf16 and fp16 gradients; one to three parameter groups with their
+own lr and weight decay; frozen and non-owned tensors; empty tensors; buffers
+at element offsets that leave p, m, v and g with or without a common 16-byte
+alignment; bf16 and fp16 working copies; an on-device lr schedule per group;
+eager or replayed steps.  Three updates per table, everything compared.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from tensor_optimizer_step_amd import workloads as W
+
+from parity_util import assert_close, assert_norm, host, log, make_oracle
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from tensor_optimizer_step_amd import somaopt
+    somaopt.load()
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _placed(n, dtype, off):
+    """A 1-D device tensor of n elements starting `off` elements into its own
+    allocation (the guard elements before it are never handed to the library)."""
+    base = torch.zeros(n + off + 1, dtype=dtype, device="cuda")
+    return base[off:off + n]
+
+
+def _draw(seed):
+    from tensor_optimizer_step_amd import somaopt
+    rng = np.random.default_rng(9000 + seed)
+    n = int(rng.integers(6, 40))
+    sizes = np.rint(np.exp(rng.uniform(0.0, np.log(70000.0), n))).astype(int)
+    sizes[rng.random(n) < 0.08] = 0
+    n_groups = int(rng.integers(1, 4))
+    groups = [W.GroupHP(float(10.0 ** rng.uniform(-5, -3)), float(rng.choice([0.0, 0.01, 0.1])))
+              for _ in range(n_groups)]
+    dts = [W.F32, W.BF16, W.F16]
+    tensors = [W.TensorSpec(f"r{i}", int(sizes[i]), int(rng.integers(0, n_groups)),
+                            dts[int(rng.integers(0, 3))], trainable=bool(rng.random() > 0.15))
+               for i in range(n)]
+    wl = W.Workload(f"random{seed}", 1, tensors, groups, max_norm=float(rng.choice([0.5, 1.0, 100.0])),
+                    grad_divisor=float(rng.choice([1.0, 2.0, 8.0])), steps=3, g_std=0.05,
+                    nan_frozen_grads=True)
+    owner = [bool(rng.random() > 0.2) for _ in range(n)]
+    # element offsets: 0 keeps the allocation's alignment; odd offsets break it
+    offs = [[int(rng.choice([0, 0, 1, 2, 4])) for _ in range(4)] for _ in range(n)]
+    lowp = [int(rng.choice([0, 0, 1, 2])) for _ in range(n)]          # none / bf16 / f16
+    lowp_off = [int(rng.choice([0, 0, 4, 1])) for _ in range(n)]
+    kinds = [somaopt.SCHED_NONE, somaopt.SCHED_LINEAR_WARMUP, somaopt.SCHED_COSINE, somaopt.SCHED_WARMUP_COSINE]
+    scheds = []
+    for g in groups:
+        k = kinds[int(rng.integers(0, 4))]
+        w = int(rng.integers(1, 3))
+        total = int(rng.integers(w + 1, 6))
+        scheds.append((k, w, total, g.lr, float(g.lr * rng.choice([0.0, 0.1]))))
+    graph = bool(rng.random() > 0.5)
+    return wl, owner, offs, lowp, lowp_off, scheds, graph
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_table_against_oracle(seed):
+    from tensor_optimizer_step_amd.somaopt import FusedAdamW
+    wl, owner, offs, lowp_kind, lowp_off, scheds, graph = _draw(seed)
+    log(f"[random] seed {seed}: {wl.n_tensors} tensors, {wl.trainable_numel} trainable elements, "
+        f"{len(wl.groups)} groups, graph={graph}")
+    p, g, m, v, lp = [], [], [], [], []
+    for i, t in enumerate(wl.tensors):
+        p.append(_placed(t.numel, torch.float32, offs[i][0]))
+        p[-1].copy_(W.param_values(wl, i, "cuda"))
+        g.append(_placed(t.numel, W.torch_dtype(t.grad_dtype), offs[i][1]))
+        m.append(_placed(t.numel, torch.float32, offs[i][2]))
+        v.append(_placed(t.numel, torch.float32, offs[i][3]))
+        if lowp_kind[i] and t.trainable:
+            dt = torch.bfloat16 if lowp_kind[i] == 1 else torch.float16
+            lp.append(_placed(t.numel, dt, lowp_off[i]))
+            lp[-1].fill_(float("nan"))
+        else:
+            lp.append(None)
+    p0 = [host(x) for x in p]
+    frozen_before = {i: (host(p[i]), host(m[i]), host(v[i])) for i, t in enumerate(wl.tensors) if not t.trainable}
+    opt = FusedAdamW(p, g, m, v, [t.group for t in wl.tensors], wl.groups, wl.max_norm, wl.grad_divisor,
+                     trainable=[t.trainable for t in wl.tensors], owner=owner, params_lowp=lp)
+    opt.set_schedules(scheds)
+    if graph:
+        opt.capture()
+    ora = make_oracle(wl, p0, owner=owner)
+    for k in range(1, wl.steps + 1):
+        for i in range(wl.n_tensors):
+            g[i].copy_(W.grad_values(wl, i, k, "cuda"))
+        grads = [host(x) for x in g]
+        if graph:
+            opt.replay()
+        else:
+            opt.step()
+        stats, steps = opt.read_stats()
+        lrs = [O.scheduled_lr(sc[0], k, lr=grp.lr, peak=sc[3], floor=sc[4], warmup=sc[1], total=sc[2])
+               for sc, grp in zip(scheds, wl.groups)]
+        want = ora.step(grads, lrs)
+        assert_norm(stats.norm, want.norm)
+        assert steps == [k] * len(wl.groups)
+        for i, x in enumerate(g):
+            assert np.array_equal(host(x).view(np.uint8), grads[i].view(np.uint8)), f"grad {i} written"
+    torch.cuda.synchronize()
+    for i, t in enumerate(wl.tensors):
+        if not t.trainable:
+            for name, a, b in zip("pmv", (p[i], m[i], v[i]), frozen_before[i]):
+                assert np.array_equal(host(a).view(np.uint32), b.view(np.uint32)), f"frozen {name}{i}"
+            continue
+        gp = host(p[i])
+        assert_close(f"p[{i}]", gp, ora.p[i])
+        assert_close(f"m[{i}]", host(m[i]), ora.m[i])
+        assert_close(f"v[{i}]", host(v[i]), ora.v[i])
+        if lp[i] is not None:
+            got = lp[i].cpu().view(torch.int16).numpy().view(np.uint16)
+            mine = O.round_to_bf16_bits(gp) if lowp_kind[i] == 1 else O.round_to_f16(gp).view(np.uint16)
+            assert np.array_equal(got, mine), f"working copy {i}"
+    opt.close()
