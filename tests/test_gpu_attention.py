@@ -149,6 +149,27 @@ def test_attention_peaked_scores(case):
     _run_ctx_case(case, amp=4.0)
 
 
+def _random_ctx_case(seed):
+    rng = np.random.default_rng(7000 + seed)
+    share = int(rng.choice([1, 1, 2, 3]))
+    b = share * int(rng.integers(1, 4))
+    h = int(rng.integers(1, 7))
+    lq = int(rng.integers(1, 200))
+    lc = int(rng.choice([0, int(rng.integers(1, 300))]))
+    la = int(rng.integers(0 if lc else 1, 150))
+    d = int(rng.choice([64, 128]))
+    return (b, h, lq, lc, la, share, d)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_attention_random_shapes(seed):
+    """Seeded random shapes: ragged query and key counts, one or several query
+    and key blocks per (batch, head), shared or per-batch contexts, either head
+    dimension -- through the fused and the separate dK/dV paths and the
+    XCD-grouped workgroup order."""
+    _run_ctx_case(_random_ctx_case(seed))
+
+
 def _run_ctx_case(case, amp=1.0):
     from tensor_optimizer_step_amd import somaopt
     b, h, lq, lc, la, share, d = case
