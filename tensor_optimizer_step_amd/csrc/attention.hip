@@ -190,16 +190,17 @@ struct WgCoord {
 };
 __device__ __forceinline__ WgCoord xcd_grouped(int share) {
     if (share <= 1 && gridDim.x == 1) return WgCoord{(int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z};
-    const uint32_t nx = gridDim.x, nh = gridDim.y, nb = gridDim.z;
-    const uint32_t n = nx * nh * nb;
-    const uint32_t l = blockIdx.x + nx * (blockIdx.y + nh * blockIdx.z);
-    const uint32_t xcd = l % 8, local = l / 8, per = n / 8, rem = n % 8;
-    uint32_t t = xcd * per + (xcd < rem ? xcd : rem) + local;   // logical index
+    // 64-bit: a grid of up to 2^16 x 2^16 x 2^16 workgroups
+    const uint64_t nx = gridDim.x, nh = gridDim.y, nb = gridDim.z;
+    const uint64_t n = nx * nh * nb;
+    const uint64_t l = blockIdx.x + nx * (blockIdx.y + nh * (uint64_t)blockIdx.z);
+    const uint64_t xcd = l % 8, local = l / 8, per = n / 8, rem = n % 8;
+    uint64_t t = xcd * per + (xcd < rem ? xcd : rem) + local;   // logical index
     WgCoord c;
     c.x = (int)(t % nx);
     t /= nx;
-    const uint32_t sh = (uint32_t)share;
-    const uint32_t m = t % sh;
+    const uint64_t sh = (uint64_t)share;
+    const uint64_t m = t % sh;
     t /= sh;
     c.h = (int)(t % nh);
     c.b = (int)((t / nh) * sh + m);
