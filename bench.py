@@ -199,6 +199,21 @@ def cpu_baseline(wl, seconds: float) -> dict:
                       f"{len(times)} timed steps, median step {med:.3f} s, NumPy float64, one thread"}
 
 
+def attention_hash() -> str:
+    src = os.path.join(ROOT, "tensor_optimizer_step_amd", "csrc", "attention.hip")
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+
+
+def load_attention_traffic():
+    """HBM bytes per forward launch from committed rocprofv3 counters, if they
+    were taken on the current attention source; else None."""
+    path = os.path.join(TRAFFIC_DIR, "traffic_attn_fwd_frozen_attention.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    return rec.get("hbm_bytes_per_launch") if rec.get("kernel_sha256_16") == attention_hash() else None
+
+
 def load_traffic(workload: str, algo_bytes: int):
     """HBM bytes per update-pass launch from committed rocprofv3 counters, if they
     were taken on the current kernel source; else None."""
@@ -476,8 +491,8 @@ def attention_bench(torch, args):
         "backward_all_keys_trainable": {"ms": ms_ball, "TFLOPs": flops_ball / ms_ball / 1e9,
                                         "note": "one input set"},
         "roofline": {"bound": "hbm", "achieved": round(bytes_f / ms_f / 1e6, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(bytes_f / ms_f / 1e6 / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "attn_fwd"},
+                     "unit": "GB/s", "frac": round(bytes_f / ms_f / 1e6 / HBM_PEAK_GBS, 4),
+                     "traffic": load_attention_traffic(), "kernel": "attn_fwd"},
         "cpu_baseline": (cpu_baseline_attention(torch, sh, args.cpu_seconds) if args.cpu_seconds > 0 else None),
         "wall_s": wall,
     }
@@ -563,7 +578,7 @@ def arrival_bench(torch, args, wl, opt, keep, stream, bts):
         "roofline": {"bound": "hbm", "kernel": "adamw_pass2",
                      "achieved": round(bts["pass2"] / (upd_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(bts["pass2"] / (upd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": None, "avg_launch_ms": round(upd_ms, 5),
+                     "traffic": load_traffic(wl.name, bts["pass2"]), "avg_launch_ms": round(upd_ms, 5),
                      "arrival_call_avg_ms": round(arr_ms, 5),
                      "arrival_call_GBps": round(arrival_bytes / (arr_ms * 1e-3) / 1e9, 1)},
         "cpu_baseline": (cpu_baseline_arrival(wl, args.cpu_seconds, acc) if args.cpu_seconds > 0 else None),
