@@ -685,7 +685,8 @@ def main():
         raise RuntimeError("non-finite statistics in the benchmark run")
 
     p2_gbs = bts["pass2"] / (p2_ms * 1e-3) / 1e9
-    traffic = load_traffic(wl.name, bts["pass2"]) if args.lowp == "none" else None
+    traffic = (load_traffic(wl.name + ("" if args.lowp == "none" else "_" + args.lowp), bts["pass2"])
+               if args.lowp in ("none", "bf16") else None)
     roofline = {"bound": "hbm", "achieved": round(p2_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(p2_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "adamw_pass2", "algorithmic_bytes_per_launch": bts["pass2"],
