@@ -149,6 +149,15 @@ def test_attention_peaked_scores(case):
     _run_ctx_case(case, amp=4.0)
 
 
+def test_attention_bench_shape_full_size():
+    """The benchmark's own shape and launch configuration (64 batches, 8 heads,
+    64 action queries, 960 frozen context keys in their own buffer, 64
+    trainable action keys, D = 128), every output element against the oracle."""
+    import bench
+    sh = bench.ATTN_SHAPE
+    _run_ctx_case((sh["batch"], sh["heads"], sh["lq"], sh["l_ctx"], sh["l_act"], 1, sh["head_dim"]))
+
+
 def _random_ctx_case(seed):
     rng = np.random.default_rng(7000 + seed)
     share = int(rng.choice([1, 1, 2, 3]))
