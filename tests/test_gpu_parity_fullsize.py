@@ -102,7 +102,15 @@ def test_backbone_7b_full_size_sampled():
     run_unsharded(W.backbone_7b())
 
 
-def run_unsharded(wl):
+def test_action_expert_full_size_bf16_working_copy():
+    """The bench's --lowp bf16 configuration at full size, three steps: sampled
+    p/m/v against the oracle, and every element of every working copy equal to
+    torch's round-to-nearest-even conversion of the kernel's fp32 master."""
+    from dataclasses import replace
+    run_unsharded(replace(W.action_expert(), steps=3), lowp=torch.bfloat16)
+
+
+def run_unsharded(wl, lowp=None):
     from tensor_optimizer_step_amd.somaopt import FusedAdamW
     log(f"[fullsize] {wl.name}: {wl.n_tensors} tensors, {wl.trainable_numel} elements")
     rng = np.random.default_rng(7)
@@ -115,8 +123,9 @@ def run_unsharded(wl):
         v.append(torch.zeros(t.numel, device=dev))
     idx = [sample_indices(t.numel, rng) for t in wl.tensors]
     ora = SampledOracle(wl, [_gather(x, ix).numpy() for x, ix in zip(p, idx)], idx)
+    lp = [torch.empty(t.numel, dtype=lowp, device=dev) for t in wl.tensors] if lowp is not None else None
     opt = FusedAdamW(p, g, m, v, [t.group for t in wl.tensors], wl.groups, wl.max_norm,
-                     wl.grad_divisor)
+                     wl.grad_divisor, params_lowp=lp)
     opt.capture()
     sumsq_cache = {}
     for k in range(1, wl.steps + 1):
@@ -145,8 +154,12 @@ def run_unsharded(wl):
         for j, (dev_t, want) in enumerate(((p[i], ora.p[i]), (m[i], ora.m[i]), (v[i], ora.v[i]))):
             worst[j] = max(worst[j], assert_close(f"{'pmv'[j]}[{i}]", _gather(dev_t, idx[i]).numpy(), want))
     log(f"[fullsize] {wl.name}: tensor-wise rel err p={worst[0]:.2e} m={worst[1]:.2e} v={worst[2]:.2e}")
+    if lp is not None:
+        for i in range(wl.n_tensors):
+            assert torch.equal(lp[i].view(torch.int16), p[i].to(lowp).view(torch.int16)), f"working copy {i}"
+        log(f"[fullsize] {wl.name}: every working-copy element equals the rounding of its fp32 master")
     opt.close()
-    del p, g, m, v
+    del p, g, m, v, lp
 
 
 def test_sharded_7b_full_size_sampled():
