@@ -214,16 +214,17 @@ def load_attention_traffic():
     return rec.get("hbm_bytes_per_launch") if rec.get("kernel_sha256_16") == attention_hash() else None
 
 
-def load_traffic(workload: str, algo_bytes: int):
-    """HBM bytes per update-pass launch from committed rocprofv3 counters, if they
-    were taken on the current kernel source; else None."""
+def load_traffic(workload: str, launches_per_pass: int):
+    """HBM bytes per update pass (the sum over its launches) from committed
+    rocprofv3 counters, if they were taken on the current kernel source with the
+    same split into launches; else None."""
     path = os.path.join(TRAFFIC_DIR, f"traffic_pass2_{workload}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_sha256_16") != kernel_hash():
+    if rec.get("kernel_sha256_16") != kernel_hash() or rec.get("launches_per_pass", 1) != launches_per_pass:
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec.get("hbm_bytes_per_pass", rec.get("hbm_bytes_per_launch"))
 
 
 def device_schedules(somaopt, wl):
@@ -556,6 +557,7 @@ def arrival_bench(torch, args, wl, opt, keep, stream, bts):
     torch.cuda.synchronize()
     arr_ms = sum(x.elapsed_time(y) for x, y, _ in ev) / len(ev)
     upd_ms = sum(y.elapsed_time(z) for _, y, z in ev) / len(ev)
+    n_launch = int(opt.plan_info().pass2_launches)
     stats, _ = opt.read_stats()
     if not all(math.isfinite(x) for x in (stats.norm, stats.clip_coef)):
         raise RuntimeError("non-finite statistics in the benchmark run")
@@ -578,7 +580,8 @@ def arrival_bench(torch, args, wl, opt, keep, stream, bts):
         "roofline": {"bound": "hbm", "kernel": "adamw_pass2",
                      "achieved": round(bts["pass2"] / (upd_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(bts["pass2"] / (upd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": load_traffic(wl.name, bts["pass2"]), "avg_launch_ms": round(upd_ms, 5),
+                     "traffic": load_traffic(wl.name, n_launch), "launches_per_pass": n_launch,
+                     "algorithmic_bytes_per_pass": bts["pass2"], "avg_pass_ms": round(upd_ms, 5),
                      "arrival_call_avg_ms": round(arr_ms, 5),
                      "arrival_call_GBps": round(arrival_bytes / (arr_ms * 1e-3) / 1e9, 1)},
         "cpu_baseline": (cpu_baseline_arrival(wl, args.cpu_seconds, acc) if args.cpu_seconds > 0 else None),
@@ -685,12 +688,15 @@ def main():
         raise RuntimeError("non-finite statistics in the benchmark run")
 
     p2_gbs = bts["pass2"] / (p2_ms * 1e-3) / 1e9
-    traffic = (load_traffic(wl.name + ("" if args.lowp == "none" else "_" + args.lowp), bts["pass2"])
+    n_launch = int(info.pass2_launches)
+    traffic = (load_traffic(wl.name + ("" if args.lowp == "none" else "_" + args.lowp), n_launch)
                if args.lowp in ("none", "bf16") else None)
     roofline = {"bound": "hbm", "achieved": round(p2_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(p2_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "adamw_pass2", "algorithmic_bytes_per_launch": bts["pass2"],
-                "avg_launch_ms": round(p2_ms, 5),
+                # one update pass = launches_per_pass launches back to back on one
+                # stream (1 up to 131072 workgroups); figures are per pass
+                "kernel": "adamw_pass2", "launches_per_pass": n_launch,
+                "algorithmic_bytes_per_pass": bts["pass2"], "avg_pass_ms": round(p2_ms, 5),
                 # the norm call: norm pass + fixed-order reduction + finalize
                 "norm_call_avg_ms": round(p1_ms, 5),
                 "norm_call_GBps": round(bts["pass1"] / (p1_ms * 1e-3) / 1e9, 1)}

@@ -126,6 +126,8 @@ typedef struct {
     int64_t table_bytes;        /* device bytes of the descriptor tables       */
     int64_t pass1_wg_per_cu;    /* resident norm-pass workgroups per CU (0: no limit)   */
     int64_t pass2_wg_per_cu;    /* resident update-pass workgroups per CU (0: no limit) */
+    int64_t pass2_launches;     /* launches the update pass is split into (consecutive
+                                   ranges of its workgroups, same stream; 0 if empty) */
 } somaopt_plan_info;
 
 /* One row of the host-side plan, for inspection (somaopt_debug_plan). */
@@ -171,7 +173,9 @@ typedef struct somaopt_handle somaopt_handle;
  * workgroups per compute unit (0: no limit; unset: chosen from the table
  * shape, reported in somaopt_plan_info); SOMAOPT_SEGMENT_COST,
  * SOMAOPT_UPDATE_SEGMENT_COST = elements charged per segment when short
- * segments are packed into the norm / update pass's workgroups (1024, 4096).
+ * segments are packed into the norm / update pass's workgroups (1024, 4096);
+ * SOMAOPT_PASS2_SLICE_BLOCKS = update-pass workgroups per launch above which
+ * the pass is split into several launches (131072; 0: always one launch).
  */
 int somaopt_init_tensor_table(const somaopt_tensor_desc* descs, int64_t n_tensors,
                               const somaopt_group* groups, int32_t n_groups,
@@ -192,9 +196,11 @@ int somaopt_init_tensor_table(const somaopt_tensor_desc* descs, int64_t n_tensor
 int somaopt_grad_sqnorm(somaopt_handle* h, void* stream);
 
 /*
- * Update pass: one launch over every trainable segment; reads g, p, m, v and
- * writes p, m, v using the statistics the preceding somaopt_grad_sqnorm left
- * on the device.  Landing page, paragraph 8: the last pass works from the
+ * Update pass: one launch over every trainable segment (a pass of more than
+ * 131072 workgroups, about 5.4e8 elements, goes out as consecutive launches
+ * over ranges of its workgroups, each still spanning many tensors: see
+ * somaopt_plan_info.pass2_launches); reads g, p, m, v and writes p, m, v using
+ * the statistics the preceding somaopt_grad_sqnorm left on the device.  Landing page, paragraph 8: the last pass works from the
  * unmodified gradients and does normalization, clipping and AdamW at once.
  * SOMAOPT_E_STATE if no somaopt_grad_sqnorm preceded it since the last update.
  */

@@ -28,6 +28,25 @@ constexpr int kVecsPerThread = 4;
 constexpr int kPass1WgPerCuStreaming = 6;
 constexpr int kPass2WgPerCuStreaming = 2;
 constexpr int kPass2WgPerCuPacked = 4;
+// Workgroups per update-pass launch.  A larger pass is split into consecutive
+// launches of about this many workgroups each, on the same stream.  The
+// hardware deals workgroups to the 8 XCDs in turn and each XCD then works
+// through its share at its own pace; over a long launch the XCDs drift apart,
+// so the single front of addresses that all CUs stream through splits into
+// eight, and DRAM rows whose data is spread over several XCDs' workgroups are
+// opened more than once.  A launch boundary brings the XCDs back together.
+// Measured on MI355X over 6.7e9 elements (1.65M workgroups, 28.9 ms in one
+// launch): 27.72 ms at 131072 per launch, 27.70 at 65536, 27.97 at 16384 (each
+// boundary costs about 4 us of ramp-down and ramp-up); a 302M-element table
+// (73,780 workgroups) is unchanged by splitting, so it stays one launch.
+constexpr uint32_t kPass2SliceBlocks = 131072;
+// Number of launches for `n_blocks` workgroups at `per_launch` per launch
+// (0: one launch); every launch gets the same count, the last possibly fewer.
+inline int64_t update_launches(int64_t n_blocks, int64_t per_launch) {
+    if (n_blocks <= 0) return 0;
+    if (per_launch <= 0 || n_blocks <= per_launch) return 1;
+    return (n_blocks + per_launch - 1) / per_launch;
+}
 // LDS bytes to reserve per workgroup for `wg_per_cu` resident workgroups on a
 // CU with `lds_per_cu` bytes (2 KiB granules, so that allocation rounding
 // never lowers the count); 0 if the device reports no LDS size.

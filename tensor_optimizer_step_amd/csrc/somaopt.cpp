@@ -6,6 +6,7 @@
 // in the kernels (kernels.hip).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -208,6 +209,7 @@ void fill_info(somaopt_plan_info* info, int64_t n_tensors, const Counts& c, cons
                                   (p1.block_first.size() + p2.block_first.size()) * sizeof(uint32_t));
     info->pass1_wg_per_cu = streaming_plan(p1) ? kPass1WgPerCuStreaming : 0;
     info->pass2_wg_per_cu = streaming_plan(p2) ? kPass2WgPerCuStreaming : kPass2WgPerCuPacked;
+    info->pass2_launches = update_launches(p2.n_blocks(), kPass2SliceBlocks);
 }
 
 int launch_norm_pass(somaopt_handle* h, int advance, hipStream_t s) {
@@ -225,16 +227,24 @@ int launch_norm_pass(somaopt_handle* h, int advance, hipStream_t s) {
     return e == hipSuccess ? SOMAOPT_OK : hip_fail(e, "norm pass launch");
 }
 
+// The update pass as info.pass2_launches launches over consecutive ranges of
+// its workgroups.  A launch over workgroups [first, first + n) reads
+// blk_first[first .. first + n], inside the nblk2 + 1 entries of the table.
 int launch_update_pass(somaopt_handle* h, hipStream_t s) {
     if (h->nblk2 == 0) return SOMAOPT_OK;
+    const uint32_t nl = (uint32_t)std::max<int64_t>(h->info.pass2_launches, 1);
+    const uint32_t per = (h->nblk2 + nl - 1) / nl;
     Pass2Args a;
     a.segs = h->d_seg2;
-    a.blk_first = h->d_blk2;
-    a.n_blocks = h->nblk2;
     a.state = h->d_state;
     a.lds_bytes = h->lds2;
-    hipError_t e = launch_pass2(a, s);
-    return e == hipSuccess ? SOMAOPT_OK : hip_fail(e, "update pass launch");
+    for (uint32_t first = 0; first < h->nblk2; first += per) {
+        a.blk_first = h->d_blk2 + first;
+        a.n_blocks = std::min(per, h->nblk2 - first);
+        hipError_t e = launch_pass2(a, s);
+        if (e != hipSuccess) return hip_fail(e, "update pass launch");
+    }
+    return SOMAOPT_OK;
 }
 
 }  // namespace
@@ -379,6 +389,8 @@ int somaopt_init_tensor_table(const somaopt_tensor_desc* descs, int64_t n_tensor
     if (w2 >= 0) h->info.pass2_wg_per_cu = std::min<int64_t>(w2, 64);
     h->lds1 = occupancy_lds(lds_per_cu, (int)h->info.pass1_wg_per_cu);
     h->lds2 = occupancy_lds(lds_per_cu, (int)h->info.pass2_wg_per_cu);
+    const int64_t slice = env_int("SOMAOPT_PASS2_SLICE_BLOCKS", -1);
+    if (slice >= 0) h->info.pass2_launches = update_launches(h->nblk2, slice);
     hipStream_t s = static_cast<hipStream_t>(stream);
 
     if ((e = alloc_upload(&h->d_seg1, s1, s)) != hipSuccess ||

@@ -57,7 +57,7 @@ class PlanInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "n_tensors", "n_trainable", "trainable_numel", "owned_numel", "pass1_segments",
         "pass1_blocks", "pass2_segments", "pass2_blocks", "scalar_segments", "pass1_chunk",
-        "pass2_chunk", "table_bytes", "pass1_wg_per_cu", "pass2_wg_per_cu")]
+        "pass2_chunk", "table_bytes", "pass1_wg_per_cu", "pass2_wg_per_cu", "pass2_launches")]
 
     def as_dict(self) -> dict:
         return {n: getattr(self, n) for n, _ in self._fields_}

@@ -192,6 +192,19 @@ def test_occupancy_follows_the_table_shape():
     assert info.pass2_wg_per_cu == 2
 
 
+def test_update_pass_launch_split():
+    """An update pass above 131072 workgroups is split into launches of equal
+    size; at or below it stays one launch; an empty pass has none."""
+    _, info = S.debug_plan(_rows([131072 * 4096], dtypes=[S.BF16]), 1, 2)
+    assert (info.pass2_blocks, info.pass2_launches) == (131072, 1)
+    _, info = S.debug_plan(_rows([131072 * 4096 + 1], dtypes=[S.BF16]), 1, 2)
+    assert (info.pass2_blocks, info.pass2_launches) == (131073, 2)
+    _, info = S.debug_plan(_rows([100 * 4096] * 5), 1, 2)
+    assert (info.pass2_blocks, info.pass2_launches) == (500, 1)
+    _, info = S.debug_plan([], 1, 2)
+    assert info.pass2_launches == 0
+
+
 def test_plan_empty_table():
     segs, info = S.debug_plan([], 1, 2)
     assert segs == [] and info.trainable_numel == 0

@@ -644,3 +644,30 @@ def test_other_chunkings_and_two_level_reduction(chunks, monkeypatch):
     wl = W.launch_bound(n_tensors=3000)
     wl.steps = 3
     st, ora = run_and_compare(wl)
+
+
+@pytest.mark.parametrize("per_launch", [3, 100])
+def test_update_pass_split_into_launches(per_launch, monkeypatch):
+    """The update pass split into consecutive launches (the env knob, set far
+    below its default so that a small table gets many launches) equals one
+    launch bit for bit, eager and replayed."""
+    wl = W.action_expert(blocks=1, d=512, mlp=2048)
+    monkeypatch.setenv("SOMAOPT_PASS2_SLICE_BLOCKS", "0")
+    one, n_one = _run_steps(wl, 3, graph=False)
+    monkeypatch.setenv("SOMAOPT_PASS2_SLICE_BLOCKS", str(per_launch))
+    probe = make_handle(wl, allocate(wl))
+    info = probe.plan_info()
+    probe.close()
+    assert info.pass2_launches == -(-info.pass2_blocks // per_launch) > 1
+    log(f"[split] {info.pass2_blocks} update workgroups in {info.pass2_launches} launches")
+    for graph in (False, True):
+        split, n_split = _run_steps(wl, 3, graph=graph)
+        assert n_split == n_one
+        assert all(np.array_equal(x, y) for x, y in zip(one, split)), f"graph={graph}"
+
+
+def test_update_pass_split_matches_oracle(monkeypatch):
+    monkeypatch.setenv("SOMAOPT_PASS2_SLICE_BLOCKS", "2")
+    wl = W.tiny(seed_offset=5)
+    wl.steps = 3
+    run_and_compare(wl)
