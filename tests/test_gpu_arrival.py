@@ -203,10 +203,14 @@ def test_arrival_scaled_action_expert_many_workgroups():
     opt.close()
 
 
-def test_arrival_graph_replay_equals_eager_bitwise():
+@pytest.mark.parametrize("per_launch", [None, 5], ids=["one-update-launch", "split-update"])
+def test_arrival_graph_replay_equals_eager_bitwise(per_launch, monkeypatch):
     """{arrival, update} captured once and replayed equals the eager calls bit
     for bit, on two identical states; every replay is checked (several replays
-    with host synchronization between them)."""
+    with host synchronization between them).  With `per_launch` the update
+    pass goes out as several launches inside the captured step."""
+    if per_launch is not None:
+        monkeypatch.setenv("SOMAOPT_PASS2_SLICE_BLOCKS", str(per_launch))
     wl = _workload([W.BF16, W.F32], seed_offset=31, n=30)
     states, opts, incs = [], [], []
     for graph in (False, True):
@@ -217,6 +221,8 @@ def test_arrival_graph_replay_equals_eager_bitwise():
         opt.register_arrival(inc)
         if graph:
             opt.capture_arrival(True)
+            if per_launch is not None:
+                assert opt.plan_info().pass2_launches > 1
         states.append(st)
         opts.append(opt)
         incs.append(inc)

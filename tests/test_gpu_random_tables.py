@@ -5,7 +5,8 @@ time: fp32, bf16 and fp16 gradients; one to three parameter groups with their
 own lr and weight decay; frozen and non-owned tensors; empty tensors; buffers
 at element offsets that leave p, m, v and g with or without a common 16-byte
 alignment; bf16 and fp16 working copies; an on-device lr schedule per group;
-eager or replayed steps.  Three updates per table, everything compared.
+eager or replayed steps; on half of the seeds an update pass split into many
+launches.  Three updates per table, everything compared.
 """
 import numpy as np
 import pytest
@@ -70,12 +71,19 @@ def _draw(seed):
     return wl, owner, offs, lowp, lowp_off, scheds, graph
 
 
+# update workgroups per launch for each seed (None: the default, one launch at
+# these sizes); small values split the update pass into many launches
+PER_LAUNCH = [None, 1, None, 7, None, 33, None, 2]
+
+
 @pytest.mark.parametrize("seed", range(8))
-def test_random_table_against_oracle(seed):
+def test_random_table_against_oracle(seed, monkeypatch):
     from tensor_optimizer_step_amd.somaopt import FusedAdamW
     wl, owner, offs, lowp_kind, lowp_off, scheds, graph = _draw(seed)
+    if PER_LAUNCH[seed] is not None:
+        monkeypatch.setenv("SOMAOPT_PASS2_SLICE_BLOCKS", str(PER_LAUNCH[seed]))
     log(f"[random] seed {seed}: {wl.n_tensors} tensors, {wl.trainable_numel} trainable elements, "
-        f"{len(wl.groups)} groups, graph={graph}")
+        f"{len(wl.groups)} groups, graph={graph}, update workgroups per launch {PER_LAUNCH[seed] or 'default'}")
     p, g, m, v, lp = [], [], [], [], []
     for i, t in enumerate(wl.tensors):
         p.append(_placed(t.numel, torch.float32, offs[i][0]))
