@@ -3,7 +3,9 @@
 One step = the whole hot path over one synthetic batch of gradients: the norm
 pass (owned fp64 sum of squares + on-device clip decision) and the fused
 update pass, replayed from the captured HIP graph.  Inputs are resident in HBM
-before the timed region starts.
+before the timed region starts.  The unsharded workloads hold p, g, m and v in
+one buffer per kind, every tensor a view at consecutive offsets (--layout
+tensor: one allocation per tensor and kind instead).
 
 Prints ONE JSON line.  ``value`` is trainable param-elements updated per
 second; the line also carries the achieved model GB/s, the roofline of the
@@ -11,6 +13,7 @@ dominant kernel (the update pass, HBM-bound) measured with HIP events on the
 stream it is launched on, and the fp64 CPU oracle timed on a bounded sample.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 20] [--workload action_expert]
+                    [--layout arena|tensor]
 """
 from __future__ import annotations
 
@@ -54,6 +57,10 @@ def parse():
                     help="also time, for context only, a plain device copy of the update pass's "
                          "byte count and torch's own clip_grad_norm_ + AdamW(fused=True) on the "
                          "same shapes (fp32 gradients, which torch's AdamW requires)")
+    ap.add_argument("--layout", choices=["arena", "tensor"], default="arena",
+                    help="unsharded workloads: one buffer per kind (p, g, m, v) with the tensors as "
+                         "consecutive views at 64-element boundaries (default), or one allocation "
+                         "per tensor and kind")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for HBM counter scaling)")
     return ap.parse_args()
@@ -306,16 +313,36 @@ def cpu_baseline_attention(torch, shape: dict, seconds: float) -> dict:
                       f"{med:.3f} s, scaled by {b * h}/{pairs}; NumPy float64, BLAS on one thread"}
 
 
-def plain_setup(torch, somaopt, W, wl, dev, stream, lowp_dtype):
-    """One allocation per tensor: seeded fp32 weights, zero moments, step-1 grads."""
-    print(f"[bench] {wl.name}: {wl.n_tensors} tensors, {wl.trainable_numel} trainable elements",
-          file=sys.stderr, flush=True)
+def plain_setup(torch, somaopt, W, wl, dev, stream, lowp_dtype, layout="arena"):
+    """Seeded fp32 weights, zero moments, step-1 grads: one allocation per tensor
+    and kind, or (layout "arena") one buffer per kind holding every tensor."""
+    print(f"[bench] {wl.name}: {wl.n_tensors} tensors, {wl.trainable_numel} trainable elements, "
+          f"{layout} layout", file=sys.stderr, flush=True)
     p, g, m, v = [], [], [], []
-    for i, t in enumerate(wl.tensors):
-        p.append(W.param_values(wl, i, dev))
-        g.append(W.grad_values(wl, i, 1, dev))
-        m.append(torch.zeros(t.numel, device=dev))
-        v.append(torch.zeros(t.numel, device=dev))
+    if layout == "arena":
+        # every tensor starts at a multiple of 64 elements (256 B of fp32), as
+        # flat-buffer optimizers align them; the gaps are never touched
+        align = 64
+        offs, total = [], 0
+        for t in wl.tensors:
+            offs.append(total)
+            total += (t.numel + align - 1) // align * align
+        gdt = {W.torch_dtype(t.grad_dtype) for t in wl.tensors}
+        if len(gdt) != 1:
+            raise SystemExit("--layout arena needs one gradient dtype")
+        arena = {"p": torch.empty(total, device=dev), "g": torch.empty(total, dtype=gdt.pop(), device=dev),
+                 "m": torch.zeros(total, device=dev), "v": torch.zeros(total, device=dev)}
+        for i, t in enumerate(wl.tensors):
+            for k, lst in zip("pgmv", (p, g, m, v)):
+                lst.append(arena[k][offs[i]:offs[i] + t.numel])
+            p[-1].copy_(W.param_values(wl, i, dev))
+            g[-1].copy_(W.grad_values(wl, i, 1, dev))
+    else:
+        for i, t in enumerate(wl.tensors):
+            p.append(W.param_values(wl, i, dev))
+            g.append(W.grad_values(wl, i, 1, dev))
+            m.append(torch.zeros(t.numel, device=dev))
+            v.append(torch.zeros(t.numel, device=dev))
     lowp = None
     if lowp_dtype != "none":
         lowp = [torch.empty(t.numel, dtype=W.torch_dtype(lowp_dtype), device=dev) for t in wl.tensors]
@@ -617,7 +644,7 @@ def main():
         wl, opt, keep = sharded_setup(torch, somaopt, W, dev, stream, args.lowp)
     else:
         wl = W.WORKLOADS[args.workload]()
-        keep, opt = plain_setup(torch, somaopt, W, wl, dev, stream, args.lowp)
+        keep, opt = plain_setup(torch, somaopt, W, wl, dev, stream, args.lowp, args.layout)
     info = opt.plan_info()
     opt.capture()
     bts = bytes_per_step(wl, args.lowp != "none")
@@ -725,6 +752,7 @@ def main():
                    "model_bytes_per_step": bts["total"], "groups": len(wl.groups),
                    "pass1_blocks": info.pass1_blocks, "pass2_blocks": info.pass2_blocks,
                    "graph": True, "working_copy": args.lowp,
+                   "layout": "4 shard buffers per kind" if args.workload == "sharded_7b" else args.layout,
                    "lr_schedule": wl.schedule + ("" if wl.schedule == "constant" else
                                                  (", host setter per step" if args.host_schedule
                                                   else ", on device"))},
