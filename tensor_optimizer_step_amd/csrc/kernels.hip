@@ -288,22 +288,26 @@ __global__ __launch_bounds__(BS) void sqnorm_pass1(Pass1Args a) {
 }
 
 // Fixed-order sum of n doubles by one workgroup (valid in thread 0): thread t
-// adds elements t, t + BS, t + 2 BS, ... in increasing order, sixteen loads in
-// flight at a time, then the fixed wave/LDS tree.
+// adds elements t, t + BS, t + 2 BS, ... in increasing order, then the fixed
+// wave/LDS tree.  Sixteen loads go out together; positions past n add an
+// exact zero, so a thread with fewer than sixteen elements (every thread of
+// the first-level reduction, which sums 1024 partials with 256 threads) still
+// waits for one memory latency rather than one per element.
 template <int BS>
 __device__ __forceinline__ double fixed_order_sum(const AS_GLOBAL double* part, uint32_t n, double* lds) {
     constexpr int kLoads = 16;
     const uint32_t tid = threadIdx.x;
     double acc = 0.0;
-    uint32_t i = tid;
-    for (; i + (kLoads - 1) * BS < n; i += kLoads * BS) {
+    for (uint32_t i = tid; i < n; i += kLoads * BS) {
         double x[kLoads];
 #pragma unroll
-        for (int k = 0; k < kLoads; ++k) x[k] = part[i + k * BS];
+        for (int k = 0; k < kLoads; ++k) {
+            const uint32_t j = i + k * BS;
+            x[k] = j < n ? part[j] : 0.0;
+        }
 #pragma unroll
         for (int k = 0; k < kLoads; ++k) acc += x[k];
     }
-    for (; i < n; i += BS) acc += part[i];
     return block_sum<BS>(acc, lds);
 }
 
