@@ -295,3 +295,26 @@ def test_bench_refuses_several_gpus():
                        timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_bench_traffic_record_needs_same_kernel_and_split(tmp_path, monkeypatch):
+    """The bench reports counted HBM traffic only from a record taken on the
+    current kernel source with the same number of update launches per pass."""
+    import json
+    import sys
+    sys.path.insert(0, ROOT)
+    import bench
+    monkeypatch.setattr(bench, "TRAFFIC_DIR", str(tmp_path))
+    rec = {"kernel_sha256_16": bench.kernel_hash(), "launches_per_pass": 13, "hbm_bytes_per_pass": 12345}
+    (tmp_path / "traffic_pass2_w.json").write_text(json.dumps(rec))
+    assert bench.load_traffic("w", 13) == 12345
+    assert bench.load_traffic("w", 1) is None
+    assert bench.load_traffic("missing", 13) is None
+    rec["kernel_sha256_16"] = "0" * 16
+    (tmp_path / "traffic_pass2_w.json").write_text(json.dumps(rec))
+    assert bench.load_traffic("w", 13) is None
+    # records from before the split carry one launch per pass implicitly
+    old = {"kernel_sha256_16": bench.kernel_hash(), "hbm_bytes_per_launch": 777}
+    (tmp_path / "traffic_pass2_old.json").write_text(json.dumps(old))
+    assert bench.load_traffic("old", 1) == 777
+    assert bench.load_traffic("old", 2) is None
