@@ -314,8 +314,9 @@ def cpu_baseline_attention(torch, shape: dict, seconds: float) -> dict:
 
 
 def plain_setup(torch, somaopt, W, wl, dev, stream, lowp_dtype, layout="arena"):
-    """Seeded fp32 weights, zero moments, step-1 grads: one allocation per tensor
-    and kind, or (layout "arena") one buffer per kind holding every tensor."""
+    """Seeded fp32 weights, zero moments, step-1 grads (and the working copy, if
+    any): one allocation per tensor and kind, or (layout "arena") one buffer per
+    kind holding every tensor."""
     print(f"[bench] {wl.name}: {wl.n_tensors} tensors, {wl.trainable_numel} trainable elements, "
           f"{layout} layout", file=sys.stderr, flush=True)
     p, g, m, v = [], [], [], []
@@ -345,7 +346,12 @@ def plain_setup(torch, somaopt, W, wl, dev, stream, lowp_dtype, layout="arena"):
             v.append(torch.zeros(t.numel, device=dev))
     lowp = None
     if lowp_dtype != "none":
-        lowp = [torch.empty(t.numel, dtype=W.torch_dtype(lowp_dtype), device=dev) for t in wl.tensors]
+        ldt = W.torch_dtype(lowp_dtype)
+        if layout == "arena":
+            lbuf = torch.empty(total, dtype=ldt, device=dev)
+            lowp = [lbuf[offs[i]:offs[i] + t.numel] for i, t in enumerate(wl.tensors)]
+        else:
+            lowp = [torch.empty(t.numel, dtype=ldt, device=dev) for t in wl.tensors]
     opt = somaopt.FusedAdamW(p, g, m, v, [t.group for t in wl.tensors], wl.groups, wl.max_norm,
                              wl.grad_divisor, trainable=[t.trainable for t in wl.tensors],
                              stream=stream, params_lowp=lowp)
