@@ -94,8 +94,9 @@ def _gather(t, idx):
     return t[torch.as_tensor(idx, device=t.device)].cpu()
 
 
-def test_action_expert_full_size_sampled():
-    run_unsharded(W.action_expert())
+@pytest.mark.parametrize("layout", ["arena", "tensor"])
+def test_action_expert_full_size_sampled(layout):
+    run_unsharded(W.action_expert(), layout=layout)
 
 
 def test_backbone_7b_full_size_sampled():
@@ -110,20 +111,43 @@ def test_action_expert_full_size_bf16_working_copy():
     run_unsharded(replace(W.action_expert(), steps=3), lowp=torch.bfloat16)
 
 
-def run_unsharded(wl, lowp=None):
+def _state(wl, dev, layout, lowp):
+    """The bench's layouts: "arena" holds each kind (p, g, m, v, working copy)
+    in one buffer with every tensor at a 64-element boundary; "tensor" makes
+    one allocation per tensor and kind."""
+    if layout == "tensor":
+        p, g, m, v = [], [], [], []
+        for i, t in enumerate(wl.tensors):
+            p.append(W.param_values(wl, i, dev))
+            g.append(W.grad_values(wl, i, 1, dev))
+            m.append(torch.zeros(t.numel, device=dev))
+            v.append(torch.zeros(t.numel, device=dev))
+        lp = [torch.empty(t.numel, dtype=lowp, device=dev) for t in wl.tensors] if lowp is not None else None
+        return p, g, m, v, lp
+    offs, total = [], 0
+    for t in wl.tensors:
+        offs.append(total)
+        total += -(-t.numel // 64) * 64
+    gdt = W.torch_dtype(wl.tensors[0].grad_dtype)
+    bufs = [torch.empty(total, device=dev), torch.empty(total, dtype=gdt, device=dev),
+            torch.zeros(total, device=dev), torch.zeros(total, device=dev)]
+    if lowp is not None:
+        bufs.append(torch.empty(total, dtype=lowp, device=dev))
+    views = [[b[o:o + t.numel] for o, t in zip(offs, wl.tensors)] for b in bufs]
+    for i in range(wl.n_tensors):
+        views[0][i].copy_(W.param_values(wl, i, dev))
+        views[1][i].copy_(W.grad_values(wl, i, 1, dev))
+    return views[0], views[1], views[2], views[3], (views[4] if lowp is not None else None)
+
+
+def run_unsharded(wl, lowp=None, layout="arena"):
     from tensor_optimizer_step_amd.somaopt import FusedAdamW
-    log(f"[fullsize] {wl.name}: {wl.n_tensors} tensors, {wl.trainable_numel} elements")
+    log(f"[fullsize] {wl.name}: {wl.n_tensors} tensors, {wl.trainable_numel} elements, {layout} layout")
     rng = np.random.default_rng(7)
     dev = "cuda"
-    p, g, m, v = [], [], [], []
-    for i, t in enumerate(wl.tensors):
-        p.append(W.param_values(wl, i, dev))
-        g.append(W.grad_values(wl, i, 1, dev))
-        m.append(torch.zeros(t.numel, device=dev))
-        v.append(torch.zeros(t.numel, device=dev))
+    p, g, m, v, lp = _state(wl, dev, layout, lowp)
     idx = [sample_indices(t.numel, rng) for t in wl.tensors]
     ora = SampledOracle(wl, [_gather(x, ix).numpy() for x, ix in zip(p, idx)], idx)
-    lp = [torch.empty(t.numel, dtype=lowp, device=dev) for t in wl.tensors] if lowp is not None else None
     opt = FusedAdamW(p, g, m, v, [t.group for t in wl.tensors], wl.groups, wl.max_norm,
                      wl.grad_divisor, params_lowp=lp)
     opt.capture()
