@@ -335,12 +335,54 @@ def pin_torch_cpu_float64():
             assert np.allclose(ora.v[i], s["exp_avg_sq"].numpy(), rtol=1e-12, atol=1e-24)
 
 
+def pin_update_elements_matches_step():
+    """update_elements, which the full-size tests use to follow sampled
+    elements, equals Oracle.step on those elements bit for bit over 10 steps:
+    divisors 3 and 16, three groups (one with eps as large as the normalized
+    gradients, so every change of the gradient's scale shows), fp32 and bf16
+    gradients, clipped and unclipped steps.  The clip coefficient given to it
+    is the one computed from ALL gradients, as the full-size tests do."""
+    rng = _rng(40)
+    groups = [OA.Group(1e-2, 0.1, 0.9, 0.999, 1e-3), OA.Group(3e-3, 0.0, 0.8, 0.99, 5e-4),
+              OA.Group(5e-3, 0.05, 0.9, 0.999, 1e-8)]
+    for divisor in (3.0, 16.0):
+        sizes = [int(rng.integers(40, 300)) for _ in range(7)]
+        group = [i % 3 for i in range(7)]
+        p0 = [rng.normal(0, 0.02, n).astype(np.float32) for n in sizes]
+        ora = OA.Oracle(p0, [True] * 7, [True] * 7, group, groups, max_norm=1.0, grad_divisor=divisor)
+        idx = [np.sort(rng.choice(n, size=17, replace=False)) for n in sizes]
+        sp = [p.astype(np.float64)[ix] for p, ix in zip(p0, idx)]
+        sm = [np.zeros(len(ix)) for ix in idx]
+        sv = [np.zeros(len(ix)) for ix in idx]
+        t = [0, 0, 0]
+        clipped = []
+        for k in range(1, 11):
+            std = 0.002 * divisor if k % 2 else 0.2 * divisor      # norm ~0.03 or ~3
+            grads = []
+            for i, n in enumerate(sizes):
+                x = rng.normal(0, std, n).astype(np.float32)
+                grads.append(_bf16_bits_from_f32(x) if i % 2 else x)
+            coef = OA.clip_coefficient(OA.global_norm(grads, [True] * 7, divisor), 1.0)
+            st = ora.step(grads)
+            assert coef == st.coef
+            clipped.append(coef < 1.0)
+            for j in range(3):
+                t[j] += 1
+            for i in range(7):
+                sp[i], sm[i], sv[i] = OA.update_elements(sp[i], sm[i], sv[i], grads[i][idx[i]], coef, divisor,
+                                                         groups[group[i]], t[group[i]])
+                assert np.array_equal(sp[i], ora.p[i][idx[i]]), (divisor, k, i, "p")
+                assert np.array_equal(sm[i], ora.m[i][idx[i]]), (divisor, k, i, "m")
+                assert np.array_equal(sv[i], ora.v[i][idx[i]]), (divisor, k, i, "v")
+        assert any(clipped) and not all(clipped)
+
+
 PINS = [pin_norm_exact_example, pin_norm_decimal_bruteforce, pin_norm_reorder_invariance,
         pin_norm_owner_shards, pin_clip_coefficient, pin_step1_closed_form,
         pin_two_step_moments, pin_constant_gradient_closed_form, pin_pure_decay,
         pin_lr_zero_is_identity, pin_bf16_widening, pin_inputs_untouched_and_frozen_skipped,
         pin_nonfinite, pin_resume_equals_continuation, pin_torch_cpu_float64, pin_fp16_widening,
-        pin_bf16_working_copy_rounding]
+        pin_bf16_working_copy_rounding, pin_update_elements_matches_step]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -419,6 +461,14 @@ def _widen_shift15(g):
     return g.astype(np.float64)
 
 
+def _update_no_divisor(p, m, v, g, coef, grad_divisor, grp, t):
+    return _REAL["update_elements"](p, m, v, g, coef, 1.0, grp, t)
+
+
+def _update_coef_twice(p, m, v, g, coef, grad_divisor, grp, t):
+    return _REAL["update_elements"](p, m, v, g, coef * coef, grad_divisor, grp, t)
+
+
 def _round_truncate(x):
     return (np.asarray(x, np.float32).view(np.uint32) >> 16).astype(np.uint16)
 
@@ -428,7 +478,8 @@ def _round_half_up(x):
     return ((u + 0x8000) >> 16).astype(np.uint16)
 
 
-_REAL = {"normalized_sumsq": OA.normalized_sumsq, "adamw_update": OA.adamw_update}
+_REAL = {"normalized_sumsq": OA.normalized_sumsq, "adamw_update": OA.adamw_update,
+         "update_elements": OA.update_elements}
 
 MUTANTS = {
     "decay_after_update": ("adamw_update", _adamw_decay_after),
@@ -446,6 +497,8 @@ MUTANTS = {
     "bf16_widen_wrong_shift": ("widen_grad", _widen_shift15),
     "bf16_round_truncates": ("round_to_bf16_bits", _round_truncate),
     "bf16_round_half_up": ("round_to_bf16_bits", _round_half_up),
+    "update_elements_divisor_dropped": ("update_elements", _update_no_divisor),
+    "update_elements_coef_twice": ("update_elements", _update_coef_twice),
 }
 
 
