@@ -222,6 +222,51 @@ def debug_plan(rows: Sequence[tuple], n_groups: int, pass_: int, pass1_chunk: in
     return list(segs)[:n], info
 
 
+def _check_layout(t, what: str, dtypes, numel: int) -> None:
+    """The library addresses a buffer as numel contiguous elements of its dtype
+    from data_ptr(): refuse anything else before a pointer is handed over."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what}: expected a torch.Tensor, got {type(t).__name__}")
+    if t.dtype not in dtypes:
+        names = ", ".join(str(d).replace("torch.", "") for d in dtypes)
+        raise TypeError(f"{what}: dtype {str(t.dtype).replace('torch.', '')}, expected {names}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: not contiguous")
+    if t.numel() != numel:
+        raise ValueError(f"{what}: {t.numel()} elements, the weight has {numel}")
+
+
+def _check_device(t, what: str, device):
+    if t.device.type != "cuda":
+        raise ValueError(f"{what}: on {t.device}, not on a GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{what}: on {t.device}, the table is on {device}")
+    return t.device
+
+
+def check_tensor_row(i: int, p, g, m, v, lowp, device):
+    """Dtype, layout, size and device of one trainable descriptor's tensors:
+    fp32 weight and moments, an fp32/bf16/fp16 gradient and an optional
+    bf16/fp16 working copy, all contiguous, all with the weight's element
+    count, all on the GPU of the rest of the table (``device``; None for the
+    first row).  Returns that GPU."""
+    import torch
+    if p is None:
+        raise ValueError(f"tensor {i}: a trainable tensor needs a weight")
+    n = p.numel() if isinstance(p, torch.Tensor) else -1
+    bufs = [(p, "param", (torch.float32,)), (m, "exp_avg", (torch.float32,)),
+            (v, "exp_avg_sq", (torch.float32,)),
+            (g, "grad", (torch.float32, torch.bfloat16, torch.float16))]
+    if lowp is not None:
+        bufs.append((lowp, "param_lowp", (torch.bfloat16, torch.float16)))
+    for t, what, dtypes in bufs:
+        _check_layout(t, f"tensor {i} {what}", dtypes, n)
+    for t, what, _ in bufs:
+        device = _check_device(t, f"tensor {i} {what}", device)
+    return device
+
+
 class FusedAdamW:
     """One somaopt handle over a table of tensors.
 
@@ -241,8 +286,15 @@ class FusedAdamW:
         n = len(params)
         trainable = [True] * n if trainable is None else list(trainable)
         owner = [True] * n if owner is None else list(owner)
+        for name, seq in (("grads", grads), ("exp_avgs", exp_avgs), ("exp_avg_sqs", exp_avg_sqs),
+                          ("group_of", group_of), ("trainable", trainable), ("owner", owner)):
+            if len(seq) != n:
+                raise ValueError(f"{name} has {len(seq)} entries, params has {n}")
+        if params_lowp is not None and len(params_lowp) != n:
+            raise ValueError(f"params_lowp has {len(params_lowp)} entries, params has {n}")
         rows = []
         self._keep = []   # references that keep the tensors alive
+        device = None
         for i in range(n):
             p, g, m, v = params[i], grads[i], exp_avgs[i], exp_avg_sqs[i]
             if not trainable[i]:
@@ -250,23 +302,32 @@ class FusedAdamW:
                              int(bool(owner[i]))))
                 continue
             lp = params_lowp[i] if params_lowp is not None else None
+            device = check_tensor_row(i, p, g, m, v, lp, device)
             rows.append((p.data_ptr(), g.data_ptr(), m.data_ptr(), v.data_ptr(), p.numel(),
                          torch_dtype_code(g), int(group_of[i]), 1, int(bool(owner[i])),
                          lp.data_ptr() if lp is not None else 0,
                          torch_dtype_code(lp) if lp is not None else 0))
             self._keep.append((p, g, m, v, lp))
+        self._grads = [grads[i] if trainable[i] else None for i in range(n)]
+        self._device = device
+        self._streams = set()   # every stream a call of this handle was given
         self.n_groups = len(groups)
         self._groups = make_groups(groups)
         descs = make_descs(rows)
         h = ctypes.c_void_p()
         _check(self._lib.somaopt_init_tensor_table(
             descs, n, self._groups, self.n_groups, float(max_norm), float(grad_divisor),
-            int(initial_step), _stream_ptr(stream), ctypes.byref(h)))
+            int(initial_step), _stream_ptr(stream), ctypes.byref(h)))   # init waits for it
         self._h = h
+
+    def _s(self, stream) -> Optional[int]:
+        p = _stream_ptr(stream)
+        self._streams.add(p)
+        return p
 
     # -- step path ---------------------------------------------------------
     def grad_sqnorm(self, stream=None) -> None:
-        _check(self._lib.somaopt_grad_sqnorm(self._h, _stream_ptr(stream)))
+        _check(self._lib.somaopt_grad_sqnorm(self._h, self._s(stream)))
 
     def register_arrival(self, incoming: Sequence, stream=None) -> None:
         """Register the buffers whose values arrive for each tensor's gradient
@@ -275,16 +336,21 @@ class FusedAdamW:
         n = len(incoming)
         arr = (ctypes.c_void_p * max(n, 1))()
         for i, t in enumerate(incoming):
+            # (a count that differs from the table's is refused by the library)
+            g = self._grads[i] if i < len(self._grads) else None
+            if t is not None and g is not None:
+                _check_layout(t, f"tensor {i} incoming", (g.dtype,), g.numel())
+                _check_device(t, f"tensor {i} incoming", g.device)
             arr[i] = None if t is None else t.data_ptr()
         self._keep.append(tuple(incoming))
-        _check(self._lib.somaopt_register_arrival(self._h, arr, n, _stream_ptr(stream)))
+        _check(self._lib.somaopt_register_arrival(self._h, arr, n, self._s(stream)))
 
     def arrival_sqnorm(self, accumulate: bool, stream=None) -> None:
         """grad <- incoming (or grad + incoming), fused with the norm pass."""
-        _check(self._lib.somaopt_arrival_sqnorm(self._h, int(bool(accumulate)), _stream_ptr(stream)))
+        _check(self._lib.somaopt_arrival_sqnorm(self._h, int(bool(accumulate)), self._s(stream)))
 
     def fused_adamw_step(self, stream=None) -> None:
-        _check(self._lib.somaopt_fused_adamw_step(self._h, _stream_ptr(stream)))
+        _check(self._lib.somaopt_fused_adamw_step(self._h, self._s(stream)))
 
     def step(self, stream=None) -> None:
         """Eager step: norm pass, then update pass."""
@@ -299,19 +365,19 @@ class FusedAdamW:
         _check(self._lib.somaopt_capture_arrival_step(self._h, int(bool(accumulate))))
 
     def replay(self, stream=None) -> None:
-        _check(self._lib.somaopt_replay_step(self._h, _stream_ptr(stream)))
+        _check(self._lib.somaopt_replay_step(self._h, self._s(stream)))
 
     # -- settings ----------------------------------------------------------
     def set_groups(self, groups: Sequence, stream=None) -> None:
         self._groups = make_groups(groups)
-        _check(self._lib.somaopt_set_groups(self._h, self._groups, len(groups), _stream_ptr(stream)))
+        _check(self._lib.somaopt_set_groups(self._h, self._groups, len(groups), self._s(stream)))
 
     def set_lrs(self, lrs: Sequence[float], stream=None) -> None:
         """Change only the groups' learning rates (a schedule step)."""
         g = self._groups
         for k, lr in enumerate(lrs):
             g[k].lr = float(lr)
-        _check(self._lib.somaopt_set_groups(self._h, g, self.n_groups, _stream_ptr(stream)))
+        _check(self._lib.somaopt_set_groups(self._h, g, self.n_groups, self._s(stream)))
 
     def set_schedules(self, schedules: Sequence, stream=None) -> None:
         """On-device lr schedule per group: each entry a dict or tuple
@@ -323,20 +389,20 @@ class FusedAdamW:
                 sc = (sc.get("kind", SCHED_NONE), sc.get("warmup", 0), sc.get("total", 0),
                       sc.get("peak_lr", 0.0), sc.get("floor_lr", 0.0))
             arr[k] = Schedule(int(sc[0]), int(sc[1]), int(sc[2]), float(sc[3]), float(sc[4]))
-        _check(self._lib.somaopt_set_schedules(self._h, arr, len(schedules), _stream_ptr(stream)))
+        _check(self._lib.somaopt_set_schedules(self._h, arr, len(schedules), self._s(stream)))
 
     def set_clip(self, max_norm: float, grad_divisor: float, stream=None) -> None:
         _check(self._lib.somaopt_set_clip(self._h, float(max_norm), float(grad_divisor),
-                                          _stream_ptr(stream)))
+                                          self._s(stream)))
 
     def set_step(self, step: int, stream=None) -> None:
-        _check(self._lib.somaopt_set_step(self._h, int(step), _stream_ptr(stream)))
+        _check(self._lib.somaopt_set_step(self._h, int(step), self._s(stream)))
 
     # -- inspection --------------------------------------------------------
     def read_stats(self, stream=None):
         st = Stats()
         steps = (ctypes.c_int64 * self.n_groups)()
-        _check(self._lib.somaopt_read_stats(self._h, ctypes.byref(st), steps, _stream_ptr(stream)))
+        _check(self._lib.somaopt_read_stats(self._h, ctypes.byref(st), steps, self._s(stream)))
         return st, list(steps)
 
     def device_stats_ptr(self) -> int:
@@ -350,10 +416,24 @@ class FusedAdamW:
         return info
 
     def close(self) -> None:
+        """Wait for the streams this handle's calls were given (the library's
+        destroy requires its work to be complete and waits for nothing
+        itself), then release the handle."""
         if getattr(self, "_h", None):
+            self._sync_streams()
             self._lib.somaopt_destroy(self._h)
             self._h = None
             self._keep = []
+
+    def _sync_streams(self) -> None:
+        import torch
+        dev = self._device if self._device is not None else torch.cuda.current_device()
+        for s in self._streams:
+            if s is None:
+                torch.cuda.default_stream(dev).synchronize()
+            else:
+                torch.cuda.ExternalStream(s, device=dev).synchronize()
+        self._streams.clear()
 
     def __del__(self):
         try:
@@ -366,6 +446,38 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _attn_check(**named) -> None:
+    """Dtype, contiguity and shape of attention buffers before their pointers
+    are handed over.  ``named`` maps a name to (tensor or None, dtype, shape);
+    None tensors are passed as NULL (the library checks when that is allowed).
+    Skipped with SOMAOPT_SKIP_POINTER_CHECK=1, like the library's own checks."""
+    if os.environ.get("SOMAOPT_SKIP_POINTER_CHECK") == "1":
+        return
+    import torch
+    given = [(name, t, dtype, shape) for name, (t, dtype, shape) in named.items() if t is not None]
+    for name, t, dtype, shape in given:
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+        if t.dtype != dtype:
+            raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name}: not contiguous")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    dev = None
+    for name, t, _, _ in given:
+        if t.device.type != "cuda" or (dev is not None and t.device != dev):
+            raise ValueError(f"{name}: on {t.device}; every buffer must be on the same GPU")
+        dev = t.device
+
+
+def _q_shape(q):
+    import torch
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q must be a 4-d tensor [batch, heads, lq, head_dim]")
+    return tuple(q.shape)
+
+
 def attn_shape(q, k, lk_frozen: int, scale: Optional[float] = None) -> AttnShape:
     """Shape of bf16 q [B, H, Lq, D] and k [B, H, Lk, D]."""
     b, h, lq, d = q.shape
@@ -375,7 +487,12 @@ def attn_shape(q, k, lk_frozen: int, scale: Optional[float] = None) -> AttnShape
 
 def attn_forward(q, k, v, o, lse, lk_frozen: int = 0, scale: Optional[float] = None, stream=None):
     """O (bf16, same shape as q) and LSE (fp32 [B, H, Lq]) of softmax attention."""
+    import torch
+    b, h, lq, d = _q_shape(q)
     sh = attn_shape(q, k, lk_frozen, scale)
+    bf, f32 = torch.bfloat16, torch.float32
+    _attn_check(q=(q, bf, (b, h, lq, d)), k=(k, bf, (b, h, sh.lk, d)), v=(v, bf, (b, h, sh.lk, d)),
+                o=(o, bf, (b, h, lq, d)), lse=(lse, f32, (b, h, lq)))
     _check(load().somaopt_attn_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                        ctypes.byref(sh), _stream_ptr(stream)))
 
@@ -383,7 +500,15 @@ def attn_forward(q, k, v, o, lse, lk_frozen: int = 0, scale: Optional[float] = N
 def attn_backward(q, k, v, o, lse, d_o, dq, dk, dv, delta, lk_frozen: int,
                   scale: Optional[float] = None, stream=None):
     """dQ for every query; dK, dV (fp32 [B, H, Lk - lk_frozen, D]) for the trainable keys."""
+    import torch
+    b, h, lq, d = _q_shape(q)
     sh = attn_shape(q, k, lk_frozen, scale)
+    bf, f32 = torch.bfloat16, torch.float32
+    lt = sh.lk - sh.lk_frozen
+    _attn_check(q=(q, bf, (b, h, lq, d)), k=(k, bf, (b, h, sh.lk, d)), v=(v, bf, (b, h, sh.lk, d)),
+                o=(o, bf, (b, h, lq, d)), lse=(lse, f32, (b, h, lq)), d_o=(d_o, bf, (b, h, lq, d)),
+                dq=(dq, f32, (b, h, lq, d)), dk=(dk, f32, (b, h, lt, d)), dv=(dv, f32, (b, h, lt, d)),
+                delta=(delta, f32, (b, h, lq)))
     _check(load().somaopt_attn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(d_o),
                                         _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta), ctypes.byref(sh),
                                         _stream_ptr(stream)))
@@ -402,7 +527,14 @@ def attn_ctx_forward(q, k_ctx, v_ctx, k_act, v_act, o, lse, ctx_share: int = 1,
                      scale: Optional[float] = None, stream=None):
     """Attention over a frozen context (shared by ``ctx_share`` consecutive query
     batches) followed by trainable action keys; either may be None."""
+    import torch
+    b, h, lq, d = _q_shape(q)
     sh = attn_ctx_shape(q, k_ctx, k_act, ctx_share, scale)
+    bf, f32 = torch.bfloat16, torch.float32
+    bc = b // max(int(ctx_share), 1)
+    _attn_check(q=(q, bf, (b, h, lq, d)), k_ctx=(k_ctx, bf, (bc, h, sh.l_ctx, d)),
+                v_ctx=(v_ctx, bf, (bc, h, sh.l_ctx, d)), k_act=(k_act, bf, (b, h, sh.l_act, d)),
+                v_act=(v_act, bf, (b, h, sh.l_act, d)), o=(o, bf, (b, h, lq, d)), lse=(lse, f32, (b, h, lq)))
     _check(load().somaopt_attn_ctx_forward(_ptr(q), _ptr(k_ctx), _ptr(v_ctx), _ptr(k_act), _ptr(v_act),
                                            _ptr(o), _ptr(lse), ctypes.byref(sh), _stream_ptr(stream)))
 
@@ -410,7 +542,17 @@ def attn_ctx_forward(q, k_ctx, v_ctx, k_act, v_act, o, lse, ctx_share: int = 1,
 def attn_ctx_backward(q, k_ctx, v_ctx, k_act, v_act, o, lse, d_o, dq, dk_act, dv_act, delta,
                       ctx_share: int = 1, scale: Optional[float] = None, stream=None):
     """dQ for every query; dK, dV (fp32, shaped like k_act) for the action keys."""
+    import torch
+    b, h, lq, d = _q_shape(q)
     sh = attn_ctx_shape(q, k_ctx, k_act, ctx_share, scale)
+    bf, f32 = torch.bfloat16, torch.float32
+    bc = b // max(int(ctx_share), 1)
+    _attn_check(q=(q, bf, (b, h, lq, d)), k_ctx=(k_ctx, bf, (bc, h, sh.l_ctx, d)),
+                v_ctx=(v_ctx, bf, (bc, h, sh.l_ctx, d)), k_act=(k_act, bf, (b, h, sh.l_act, d)),
+                v_act=(v_act, bf, (b, h, sh.l_act, d)), o=(o, bf, (b, h, lq, d)), lse=(lse, f32, (b, h, lq)),
+                d_o=(d_o, bf, (b, h, lq, d)), dq=(dq, f32, (b, h, lq, d)),
+                dk_act=(dk_act, f32, (b, h, sh.l_act, d)), dv_act=(dv_act, f32, (b, h, sh.l_act, d)),
+                delta=(delta, f32, (b, h, lq)))
     _check(load().somaopt_attn_ctx_backward(_ptr(q), _ptr(k_ctx), _ptr(v_ctx), _ptr(k_act), _ptr(v_act),
                                             _ptr(o), _ptr(lse), _ptr(d_o), _ptr(dq), _ptr(dk_act),
                                             _ptr(dv_act), _ptr(delta), ctypes.byref(sh),

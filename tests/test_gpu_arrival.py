@@ -141,10 +141,19 @@ def test_arrival_call_order_and_validation():
     inc = _incoming(wl, st, False)
     with pytest.raises(somaopt.SomaoptError, match="n_tensors differs"):
         opt.register_arrival(inc[:-1])
+    def raw_register(bufs):
+        """Through the C-ABI directly: the binding would refuse a buffer whose
+        size differs from its gradient's before the library's overlap check."""
+        arr = (somaopt.ctypes.c_void_p * len(bufs))(*[None if b is None else b.data_ptr() for b in bufs])
+        return somaopt._check(lib.somaopt_register_arrival(opt._h, arr, len(bufs), None))
+
     bad = list(inc)
     bad[2] = st.g[3]             # an arriving buffer that is another tensor's gradient
     with pytest.raises(somaopt.SomaoptError, match="overlap"):
-        opt.register_arrival(bad)
+        raw_register(bad)
+    if wl.tensors[3].numel != wl.tensors[2].numel:
+        with pytest.raises(ValueError, match="tensor 2 incoming"):
+            opt.register_arrival(bad)
     bad = list(inc)
     bad[1] = st.p[1].view(torch.bfloat16)[: wl.tensors[1].numel]
     with pytest.raises(somaopt.SomaoptError, match="overlap"):

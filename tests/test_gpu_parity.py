@@ -406,37 +406,46 @@ def test_call_order_errors():
     opt.close()
 
 
+def _raw_init(rows, groups):
+    """somaopt_init_tensor_table called through the C-ABI with raw pointers (no
+    binding checks in between); returns the status and destroys any handle."""
+    from tensor_optimizer_step_amd import somaopt as S
+    lib = S.load()
+    descs = S.make_descs(rows)
+    grp = S.make_groups(groups)
+    h = S.ctypes.c_void_p()
+    rc = lib.somaopt_init_tensor_table(descs, len(rows), grp, len(groups), 1.0, 1.0, 0, None,
+                                       S.ctypes.byref(h))
+    if h.value:
+        lib.somaopt_destroy(h)
+    return rc, S.last_error()
+
+
 def test_rejects_host_memory_and_out_of_range():
-    from tensor_optimizer_step_amd.somaopt import SomaoptError
+    """The library's own checks, reached through the raw C-ABI: host memory and
+    a buffer that runs past the end of its allocation never reach a kernel.
+    The binding refuses both earlier (a CPU tensor; a tensor whose size does
+    not match the weight's)."""
+    from tensor_optimizer_step_amd.somaopt import E_INVALID, FusedAdamW
     wl = W.tiny(seed_offset=6, n_tensors=2, max_numel=64)
     st = allocate(wl)
-    bad = st.p[0].cpu()                      # host memory is never handed to a kernel
+    bad = st.p[0].cpu()
+    n = wl.tensors[0].numel
+    rc, msg = _raw_init([(bad.data_ptr(), st.g[0].data_ptr(), st.m[0].data_ptr(), st.v[0].data_ptr(), n,
+                          0, 0, 1, 1)], wl.groups)
+    assert rc == E_INVALID and "device" in msg, msg
     from parity_util import DeviceState
-    st2 = DeviceState([bad] + st.p[1:], st.g, st.m, st.v)
-    with pytest.raises(SomaoptError, match="device"):
-        make_handle(wl, st2)
+    with pytest.raises(ValueError, match="not on a GPU"):
+        make_handle(wl, DeviceState([bad] + st.p[1:], st.g, st.m, st.v))
     # a buffer whose declared size runs past the end of its allocation is
     # rejected before any kernel could touch it (64 MiB: its own allocation)
     torch.cuda.empty_cache()
     x = torch.zeros(1 << 24, device="cuda")
-    from tensor_optimizer_step_amd.somaopt import FusedAdamW
-    with pytest.raises(SomaoptError, match="past the end"):
-        FusedAdamW([_Fake(x[-50:], 100)], [x[200:300]], [x[0:100]], [x[100:200]], [0],
-                   wl.groups, 1.0, 1.0)
-
-
-class _Fake:
-    """A tensor stand-in that claims more elements than it has."""
-
-    def __init__(self, t, n):
-        self.t, self.n = t, n
-        self.dtype = t.dtype
-
-    def data_ptr(self):
-        return self.t.data_ptr()
-
-    def numel(self):
-        return self.n
+    rc, msg = _raw_init([(x[-50:].data_ptr(), x[200:300].data_ptr(), x[0:100].data_ptr(),
+                          x[100:200].data_ptr(), 100, 0, 0, 1, 1)], wl.groups)
+    assert rc == E_INVALID and "past the end" in msg, msg
+    with pytest.raises(ValueError, match="grad: 100 elements, the weight has 50"):
+        FusedAdamW([x[-50:]], [x[200:300]], [x[0:50]], [x[100:150]], [0], wl.groups, 1.0, 1.0)
 
 
 @pytest.mark.parametrize("gdt,ldt", [(W.BF16, W.BF16), (W.F16, W.F16), (W.F32, W.BF16), (W.F16, W.BF16)])
