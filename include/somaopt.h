@@ -241,9 +241,14 @@ int somaopt_register_arrival(somaopt_handle* h, const void* const* incoming, int
 int somaopt_arrival_sqnorm(somaopt_handle* h, int32_t accumulate, void* stream);
 
 /* Replace every group's hyperparameters (n_groups must equal the handle's).
- * Enqueued as a tiny kernel whose arguments carry the values, so the host
- * array may be reused at once; a learning-rate schedule computed on the host
- * calls this before each step, so every group keeps its own schedule. */
+ * SomaSpeed landing page, paragraph 8: the fused optimizer keeps each
+ * parameter group's settings and learning-rate schedule as configured; here a
+ * group is the unit that carries lr, weight decay, betas and eps, and a
+ * schedule evaluated on the host calls this before each step with the
+ * group's new lr.  Enqueued as a tiny kernel whose arguments carry the
+ * values, so the host array may be reused at once.  SOMAOPT_E_INVALID if
+ * n_groups differs or a value is out of range (lr, weight_decay not finite;
+ * beta outside [0, 1); eps negative or not finite). */
 int somaopt_set_groups(somaopt_handle* h, const somaopt_group* groups, int32_t n_groups,
                        void* stream);
 
@@ -281,25 +286,42 @@ typedef struct {
 int somaopt_set_schedules(somaopt_handle* h, const somaopt_schedule* schedules, int32_t n_groups,
                           void* stream);
 
-/* Replace max_norm and grad_divisor (both > 0), stream ordered. */
+/* Replace max_norm and grad_divisor (both finite and > 0), stream ordered:
+ * the clip threshold of the single global clip decision (landing page,
+ * paragraph 8; the veRL page's section 4.2 clips at max_norm = 1.0) and the
+ * effective-batch divisor (paragraph 7; the veRL page divides the loss by the
+ * number of micro-batches).  Applies from the next norm or arrival pass. */
 int somaopt_set_clip(somaopt_handle* h, double max_norm, double grad_divisor, void* stream);
 
 /* Set every group's completed-update count (resume), stream ordered.  Clears
- * a pending norm pass. */
+ * a pending norm pass.  The count is the t of the bias corrections, so a
+ * resumed optimizer continues exactly where a saved one stopped (the veRL
+ * page saves optimizer checkpoints periodically).  SOMAOPT_E_INVALID if
+ * step < 0. */
 int somaopt_set_step(somaopt_handle* h, int64_t step, void* stream);
 
 /* Capture {norm pass, update pass} into a HIP graph owned by the handle
- * (captured on a private stream; nothing runs).  Replaces an earlier graph. */
+ * (captured on a private stream; nothing runs).  Replaces an earlier graph.
+ * SomaSpeed landing page, paragraph 12: learner work that repeats every step
+ * is recorded once as a graph and replayed, so a step costs one launch
+ * instead of one per kernel.  Hyperparameters, schedules and the clip settings
+ * live in device state that the captured kernels read, so they change without
+ * a new capture.  SOMAOPT_E_HIP if capture or instantiation fails. */
 int somaopt_capture_step(somaopt_handle* h);
 
 /* Capture {arrival pass with the fused norm, update pass} instead -- the step
- * of somaopt_arrival_sqnorm(accumulate) followed by somaopt_fused_adamw_step.
- * Replaces an earlier graph.  SOMAOPT_E_STATE before somaopt_register_arrival. */
+ * of somaopt_arrival_sqnorm(accumulate) followed by somaopt_fused_adamw_step
+ * (graph replay of repeated learner work, landing page, paragraph 12; the
+ * arrival of the gradient shard, paragraph 1).  Replaces an earlier graph.
+ * SOMAOPT_E_STATE before somaopt_register_arrival; SOMAOPT_E_INVALID if
+ * accumulate is not 0 or 1. */
 int somaopt_capture_arrival_step(somaopt_handle* h, int32_t accumulate);
 
 /* Launch the captured step on `stream`: one full step (norm or arrival pass
- * with its step advance, then update pass).  SOMAOPT_E_STATE if not captured
- * or if an eager norm pass is pending. */
+ * with its step advance, then update pass) in one graph launch (landing page,
+ * paragraph 12: repeated learner work replayed from a graph).  Only enqueues.
+ * SOMAOPT_E_STATE if not captured or if an eager norm pass is pending;
+ * SOMAOPT_E_HIP if the launch fails. */
 int somaopt_replay_step(somaopt_handle* h, void* stream);
 
 /* Device address of the somaopt_stats block (valid for the handle's life). */
@@ -413,8 +435,15 @@ int somaopt_attn_ctx_backward(const void* q, const void* k_ctx, const void* v_ct
                               float* dk_act, float* dv_act, float* delta, const somaopt_attn_ctx_shape* shape,
                               void* stream);
 
-/* Release the handle's device tables, graph and private stream.  Waits for
- * work the handle enqueued.  NULL is ignored. */
+/* Release the handle's device tables, graph and private stream.  NULL is
+ * ignored.  The caller must first let every call it made with the handle
+ * complete (synchronize the streams it passed, or wait on an event recorded
+ * after its last call): the handle does not track the caller's streams and
+ * destroy issues no stream or device wait of its own.  It frees device
+ * memory with hipFree, however, and the HIP runtime makes hipFree wait until
+ * all work on the device has finished, so destroy returns only once the
+ * device is idle, streams the handle never used included (on MI355X a 1 MiB
+ * hipFree returned only after an 83 ms kernel on an unrelated stream). */
 void somaopt_destroy(somaopt_handle* h);
 
 /* Message for the last failed call on this thread ("" if none). */

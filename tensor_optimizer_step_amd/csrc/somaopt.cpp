@@ -455,7 +455,7 @@ int somaopt_register_arrival(somaopt_handle* h, const void* const* incoming, int
             if (rc) return rc;
         }
     }
-    Plan p3 = build_plan(d, n_tensors, 3, h->pass1_chunk, kSegmentCost, incoming);
+    Plan p3 = build_plan(d, n_tensors, 3, arrival_chunk(h->pass1_chunk), kSegmentCost, incoming);
     if (p3.segs.size() >= 0xFFFFFFFFull || (uint64_t)p3.n_blocks() * kPass1Threads >= 0xFFFFFFFFull)
         return fail(SOMAOPT_E_INVALID, "arrival table too large for one dispatch");
     if (p3.block_first.size() < 2) p3.block_first = {0u, 0u};   // statistics even when nothing is trainable
@@ -684,8 +684,10 @@ int somaopt_get_plan_info(const somaopt_handle* h, somaopt_plan_info* out) {
 
 void somaopt_destroy(somaopt_handle* h) {
     if (!h) return;
+    // The caller has completed the work it enqueued with this handle (the
+    // header's contract) and the handle's own stream only ever captured, so
+    // nothing is waited for here; hipFree itself waits for the device.
     DeviceGuard g(h->device);
-    (void)hipDeviceSynchronize();
     free_handle(h);
 }
 
