@@ -121,6 +121,14 @@ constexpr int64_t kMaxPass2Chunk = int64_t(1) << 26;
 // at most `max_chunk`.
 int64_t normalise_chunk(int64_t requested, int64_t dflt, int64_t max_chunk = int64_t(1) << 30);
 
+// Segment length of the arrival pass: the norm pass's chunk, capped like the
+// update pass's because the arrival kernel also addresses each segment's
+// vector body through buffer resources with 32-bit byte offsets (16 bytes per
+// vector; at 2^30 fp32 elements a segment's 2^32 bytes would wrap to 0).
+inline int64_t arrival_chunk(int64_t pass1_chunk) {
+    return pass1_chunk < kMaxPass2Chunk ? pass1_chunk : kMaxPass2Chunk;
+}
+
 // True when at least half of the plan's elements lie in segments of the full
 // chunk length, i.e. most workgroups stream one long run of one tensor.
 bool streaming_plan(const Plan& p);

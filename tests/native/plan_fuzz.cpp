@@ -62,6 +62,33 @@ static void check_plan(const std::vector<somaopt_tensor_desc>& d, int pass, int6
     }
 }
 
+// The arrival pass addresses each segment's vector body (16-byte vectors of
+// the gradient and of its arriving buffer) with 32-bit buffer offsets: at the
+// largest norm-pass chunk a normaliser allows, every arrival segment must
+// still span fewer than 2^31 bytes.  Gradients may not overlap for arrival,
+// and arriving buffers sit in an arena of their own.
+static void check_arrival_offsets(const std::vector<somaopt_tensor_desc>& d, std::mt19937_64& rng) {
+    std::vector<somaopt_tensor_desc> big = d;
+    std::vector<const void*> inc(d.size(), nullptr);
+    uintptr_t ga = 6ull << 40, ia = 7ull << 40;
+    for (size_t i = 0; i < big.size(); ++i) {
+        somaopt_tensor_desc& t = big[i];
+        const int64_t gsz = grad_elem_bytes(t.grad_dtype);
+        if (rng() % 4 == 0) t.numel = (int64_t)1 << 28;   // one huge tensor in four
+        t.grad = reinterpret_cast<void*>(ga);
+        ga = (ga + gsz * (uintptr_t)t.numel + 512) & ~uintptr_t(255);
+        inc[i] = reinterpret_cast<void*>(ia + gsz * (uintptr_t)(rng() % 3));
+        ia = (ia + gsz * (uintptr_t)t.numel + 512) & ~uintptr_t(255);
+    }
+    const int64_t chunk = arrival_chunk(normalise_chunk(int64_t(1) << 40, kDefaultPass1Chunk));
+    EXPECT(chunk <= kMaxPass2Chunk, "arrival chunk %lld above the buffer-offset limit", (long long)chunk);
+    Plan p = build_plan(big.data(), (int64_t)big.size(), 3, chunk, kSegmentCost, inc.data());
+    for (const PlanSeg& g : p.segs) {
+        EXPECT(g.numel <= chunk, "arrival segment of %lld elements", (long long)g.numel);
+        EXPECT(16 * g.nvec < (int64_t(1) << 31), "arrival segment body of %lld bytes", (long long)(16 * g.nvec));
+    }
+}
+
 int main() {
     std::mt19937_64 rng(12345);
     for (int trial = 0; trial < 400; ++trial) {
@@ -100,6 +127,7 @@ int main() {
         const int64_t ch2 = normalise_chunk((int64_t)(rng() % 20000), kDefaultPass2Chunk);
         check_plan(d, 1, ch1);
         check_plan(d, 2, ch2);
+        check_arrival_offsets(d, rng);
         // a corrupted copy of the table must be rejected
         std::vector<somaopt_tensor_desc> bad = d;
         const int j = (int)(rng() % n);
