@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="action_expert",
+    ap.add_argument("--workload", default="backbone_7b",
                     choices=["action_expert", "backbone_7b", "sharded_7b", "launch_bound", "tiny",
                              "frozen_attention"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -173,37 +173,127 @@ def context_bench(torch, wl, bts: dict, our_ms: float, reps: int = 10) -> dict:
                            "this_path_speedup": round(ms_torch / our_ms, 2)}}
 
 
-def cpu_baseline(wl, seconds: float) -> dict:
-    """Time the fp64 oracle on the first tensors of the workload (bounded)."""
+def cpu_pool() -> tuple:
+    """Host threads for the oracle baseline (the process's CPU affinity, capped
+    by OMP_NUM_THREADS where it is set) and the host CPU's model name."""
+    cores = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        cores = min(cores, int(omp))
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return max(cores, 1), model
+
+
+# Pieces of at most this many elements are the units the oracle baseline hands
+# to its thread pool (the update is elementwise, so a piece is exact; the sum
+# of squares adds the pieces' partial sums in table order).  2 MB fp64
+# temporaries stay in the threads' heaps and caches: on an 8-core host 2^18
+# ran 2.2e8 elements/s against 1.4e8 at 2^20 and 0.95e8 at 2^16 or 2^22.
+CPU_PIECE = 1 << 18
+
+
+def cpu_baseline(specs, groups, max_norm: float, grad_divisor: float, values, seconds: float,
+                 what: str, budget_per_core: int = 12_000_000) -> dict:
+    """Time the fp64 oracle's whole step (owned sum of squares, clip
+    coefficient, AdamW update of every element) on a bounded sample, its
+    per-tensor work fanned out over the host's cores.
+
+    ``specs``: (numel, group, owner) of the workload's tensors in table order;
+    the sample is the first tensors up to ``budget_per_core`` elements per
+    core.  ``values(i)`` returns tensor i's (fp32 weights, gradient) as host
+    arrays."""
+    from concurrent.futures import ThreadPoolExecutor
     import numpy as np
     import oracle as O
-    from tensor_optimizer_step_amd import workloads as W
 
-    budget = 20_000_000
+    cores, model = cpu_pool()
+    budget = budget_per_core * cores
     idx, tot = [], 0
-    for i, t in enumerate(wl.tensors):
-        if not t.trainable:
+    for i, (numel, _, _) in enumerate(specs):
+        if numel == 0:
             continue
-        if idx and tot + t.numel > budget:
+        if idx and tot + numel > budget:
             break
         idx.append(i)
-        tot += t.numel
-    p0 = [W.param_values(wl, i).numpy() for i in idx]
-    grads = [W.to_numpy_grad(W.grad_values(wl, i, 1)) for i in idx]
-    ora = O.Oracle(p0, [True] * len(idx), [True] * len(idx), [wl.tensors[i].group for i in idx],
-                   [O.Group(h.lr, h.weight_decay, h.beta1, h.beta2, h.eps) for h in wl.groups],
-                   wl.max_norm, wl.grad_divisor)
-    ora.step(grads)                    # untimed warm-up (page faults)
-    times = []
-    t_start = time.perf_counter()
-    while len(times) < 3 or time.perf_counter() - t_start < seconds:
-        t0 = time.perf_counter()
-        ora.step(grads)
-        times.append(time.perf_counter() - t0)
+        tot += numel
+    grp = [O.Group(h.lr, h.weight_decay, h.beta1, h.beta2, h.eps) for h in groups]
+    pieces = []          # (tensor, start, stop)
+    state = {}
+    for i in idx:
+        p0, g = values(i)
+        state[i] = [np.asarray(p0, np.float64), np.zeros(len(p0)), np.zeros(len(p0)), g]
+        for s in range(0, specs[i][0], CPU_PIECE):
+            pieces.append((i, s, min(s + CPU_PIECE, specs[i][0])))
+    t_count = [0] * len(grp)
+
+    def sumsq(piece):
+        i, a, b = piece
+        return O.normalized_sumsq([state[i][3][a:b]], [bool(specs[i][2])], grad_divisor)
+
+    def update(piece, coef):
+        i, a, b = piece
+        st = state[i]
+        k = specs[i][1]
+        st[0][a:b], st[1][a:b], st[2][a:b] = O.update_elements(
+            st[0][a:b], st[1][a:b], st[2][a:b], st[3][a:b], coef, grad_divisor, grp[k], t_count[k])
+
+    with ThreadPoolExecutor(cores) as ex:
+        def step():
+            parts = list(ex.map(sumsq, pieces))
+            total = 0.0
+            for x in parts:          # fixed table order
+                total += x
+            coef = O.clip_coefficient(float(np.sqrt(total)), max_norm)
+            for k in range(len(t_count)):
+                t_count[k] += 1
+            list(ex.map(lambda q: update(q, coef), pieces))
+
+        step()                         # untimed warm-up (page faults)
+        times = []
+        t_start = time.perf_counter()
+        while len(times) < 3 or time.perf_counter() - t_start < seconds:
+            t0 = time.perf_counter()
+            step()
+            times.append(time.perf_counter() - t0)
     med = sorted(times)[len(times) // 2]
-    return {"value": tot / med, "unit": "param-elements/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {len(idx)} tensors of {wl.name} ({tot} elements), "
-                      f"{len(times)} timed steps, median step {med:.3f} s, NumPy float64, one thread"}
+    return {"value": tot / med, "unit": "param-elements/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {len(idx)} tensors of {what} ({tot} elements), {len(times)} timed steps "
+                      f"(owned sum of squares, clip coefficient, AdamW update), median step {med:.3f} s; "
+                      f"NumPy float64, pieces of <= {CPU_PIECE} elements on a pool of {cores} threads; "
+                      f"host CPU: {model}"}
+
+
+def cpu_baseline_workload(wl, seconds: float) -> dict:
+    from tensor_optimizer_step_amd import workloads as W
+    specs = [(t.numel if t.trainable else 0, t.group, True) for t in wl.tensors]
+
+    def values(i):
+        return W.param_values(wl, i).numpy(), W.to_numpy_grad(W.grad_values(wl, i, 1))
+    return cpu_baseline(specs, wl.groups, wl.max_norm, wl.grad_divisor, values, seconds, wl.name)
+
+
+def cpu_baseline_sharded(seconds: float) -> dict:
+    """The sharded 7B table: its first descriptors (pieces of shard 0 in
+    descriptor order, owner flags as in the table)."""
+    from tensor_optimizer_step_amd import workloads as W
+    lay = W.sharded_7b()
+    base = lay.base
+    specs = [(q.numel, base.tensors[q.tensor].group, q.owner) for q in lay.pieces]
+
+    def values(j):
+        q = lay.pieces[j]
+        sl = slice(q.t_offset, q.t_offset + q.numel)
+        return (W.param_values(base, q.tensor)[sl].numpy(),
+                W.to_numpy_grad(W.grad_values(base, q.tensor, 1)[sl]))
+    return cpu_baseline(specs, base.groups, base.max_norm, base.grad_divisor, values, seconds,
+                        "sharded_7b (descriptor order)")
 
 
 def attention_hash() -> str:
@@ -734,8 +824,9 @@ def main():
                 "norm_call_avg_ms": round(p1_ms, 5),
                 "norm_call_GBps": round(bts["pass1"] / (p1_ms * 1e-3) / 1e9, 1)}
     cpu = None
-    if args.cpu_seconds > 0 and args.workload != "sharded_7b":
-        cpu = cpu_baseline(wl, args.cpu_seconds)
+    if args.cpu_seconds > 0:
+        cpu = (cpu_baseline_sharded(args.cpu_seconds) if args.workload == "sharded_7b"
+               else cpu_baseline_workload(wl, args.cpu_seconds))
     model_gbs = bts["total"] / step_s / 1e9
     out = {
         "metric": METRIC,
