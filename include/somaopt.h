@@ -183,6 +183,37 @@ int somaopt_init_tensor_table(const somaopt_tensor_desc* descs, int64_t n_tensor
                               void* stream, somaopt_handle** out);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * table build as somaopt_init_tensor_table, with the same arguments, errors
+ * and resulting handle, except that every device buffer of the handle (the
+ * norm- and update-pass tables, the per-workgroup partials and the optimizer
+ * state block) is carved from a per-device scratch array inside the library
+ * instead of being allocated.  The call makes no hipMalloc, hipFree or other
+ * device allocation (it uploads the tables with hipMemcpyAsync on `stream`
+ * and waits for that stream, like the allocating call).
+ *   - Limit: the array holds 32 MiB (33,554,432 bytes) per device, held from
+ *     the first use until the process ends.  That fits tables of about 1.5e9
+ *     elements in large tensors (the 302M-element action head needs 3.9 MB);
+ *     a table that needs more is refused with SOMAOPT_E_INVALID and a message
+ *     giving both sizes, before anything touches the device.
+ *   - Sharing: every no-allocation handle of a device uses the same array.
+ *     Each successful call overwrites it and supersedes the no-allocation
+ *     handles built before it on that device: from then on every call on an
+ *     older one returns SOMAOPT_E_STATE ("superseded"); only
+ *     somaopt_destroy is still allowed.  Work still in flight from an older
+ *     handle races with the new build: let it complete first (calls that
+ *     overlap on one device race).
+ *   - The other calls that allocate (somaopt_capture_step, the arrival
+ *     registration) keep allocating when used on such a handle;
+ *     somaopt_destroy frees nothing in the array.
+ */
+int somaopt_init_tensor_table_noalloc(const somaopt_tensor_desc* descs, int64_t n_tensors,
+                                      const somaopt_group* groups, int32_t n_groups,
+                                      double max_norm, double grad_divisor, int64_t initial_step,
+                                      void* stream, somaopt_handle** out);
+
+/*
  * Norm pass: one launch over every owned gradient segment (fp64 sum of
  * squares per workgroup), then a one-workgroup finalize kernel on the same
  * stream (no host sync) that adds the partials in a fixed order and derives the

@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsomaopt.so")
 ARCH = os.environ.get("SOMAOPT_ARCH", "gfx950")
 
-SOURCES = ["plan.cpp", "somaopt.cpp", "kernels.hip", "attention_api.cpp", "attention.hip"]
+SOURCES = ["plan.cpp", "somaopt.cpp", "kernels.hip", "attention_api.cpp", "attention.hip", "noalloc.hip"]
 
 
 def hipcc() -> str:

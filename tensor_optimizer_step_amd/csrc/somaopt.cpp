@@ -16,6 +16,7 @@
 
 #include "kernels.hpp"
 #include "plan.hpp"
+#include "scratch.hpp"
 #include "somaopt.h"
 #include "state.hpp"
 
@@ -52,6 +53,11 @@ struct somaopt_handle {
     bool pending = false;          // a norm pass opened an update not yet applied
     hipStream_t cap_stream = nullptr;
     hipGraphExec_t exec = nullptr;
+    // Built by somaopt_init_tensor_table_noalloc: the tables, partials and
+    // state live in the device scratch array (never freed), valid while the
+    // device's scratch generation is still this one.
+    bool scratch = false;
+    uint64_t scratch_gen = 0;
 };
 
 namespace {
@@ -173,21 +179,56 @@ void free_handle(somaopt_handle* h) {
     if (!h) return;
     if (h->exec) (void)hipGraphExecDestroy(h->exec);
     if (h->cap_stream) (void)hipStreamDestroy(h->cap_stream);
-    void* bufs[] = {h->d_seg1,     h->d_blk1,     h->d_seg2,        h->d_blk2,         h->d_partials,
-                    h->d_partials2, h->d_state, h->d_seg3,        h->d_blk3,         h->d_partials3,
-                    h->d_partials3b};
-    for (void* p : bufs)
+    void* init_bufs[] = {h->d_seg1, h->d_blk1, h->d_seg2, h->d_blk2, h->d_partials, h->d_partials2, h->d_state};
+    if (!h->scratch)
+        for (void* p : init_bufs)
+            if (p) (void)hipFree(p);
+    void* arrival_bufs[] = {h->d_seg3, h->d_blk3, h->d_partials3, h->d_partials3b};
+    for (void* p : arrival_bufs)
         if (p) (void)hipFree(p);
     delete h;
 }
 
+// NULL, or a no-allocation handle whose scratch tables a later no-allocation
+// init on the same device has overwritten: refused before any work.
+int check_handle(const somaopt_handle* h) {
+    if (!h) return fail(SOMAOPT_E_INVALID, "handle is NULL");
+    if (h->scratch && h->scratch_gen != scratch_generation(h->device))
+        return fail(SOMAOPT_E_STATE,
+                    "superseded: a later somaopt_init_tensor_table_noalloc on this device has overwritten the "
+                    "device scratch array that held this handle's tables");
+    return SOMAOPT_OK;
+}
+
+// Where the device buffers of a table build go: hipMalloc per buffer, or
+// consecutive 256-byte-aligned pieces of a region (the scratch array); in
+// counting mode (no region, counting = true) only the bytes are added up.
+struct Placer {
+    char* region = nullptr;
+    bool counting = false;
+    size_t used = 0;
+    hipError_t get(void** dst, size_t bytes) {
+        if (!region && !counting) return hipMalloc(dst, bytes);
+        used = (used + 255) & ~size_t(255);
+        *dst = region ? region + used : nullptr;
+        used += bytes;
+        return hipSuccess;
+    }
+};
+
 template <typename T>
-hipError_t alloc_upload(T** dst, const std::vector<T>& src, hipStream_t s) {
+hipError_t alloc_upload(T** dst, const std::vector<T>& src, hipStream_t s, Placer& where) {
     const size_t bytes = std::max<size_t>(src.size(), 1) * sizeof(T);
-    hipError_t e = hipMalloc(reinterpret_cast<void**>(dst), bytes);
-    if (e != hipSuccess) return e;
+    hipError_t e = where.get(reinterpret_cast<void**>(dst), bytes);
+    if (e != hipSuccess || where.counting) return e;
     if (!src.empty()) e = hipMemcpyAsync(*dst, src.data(), src.size() * sizeof(T), hipMemcpyHostToDevice, s);
     return e;
+}
+
+template <typename T>
+hipError_t alloc_upload(T** dst, const std::vector<T>& src, hipStream_t s) {
+    Placer malloc_each;
+    return alloc_upload(dst, src, s, malloc_each);
 }
 
 void fill_info(somaopt_plan_info* info, int64_t n_tensors, const Counts& c, const Plan& p1, const Plan& p2) {
@@ -296,6 +337,18 @@ int somaopt_init_tensor_table(const somaopt_tensor_desc* descs, int64_t n_tensor
                               const somaopt_group* groups, int32_t n_groups, double max_norm,
                               double grad_divisor, int64_t initial_step, void* stream,
                               somaopt_handle** out) {
+    return init_table(descs, n_tensors, groups, n_groups, max_norm, grad_divisor, initial_step, stream, out,
+                      false);
+}
+
+}  // extern "C"
+
+// The table build behind both init calls.  With from_scratch, every device
+// buffer is a piece of the scratch array: the bytes are counted first and a
+// table that does not fit is refused before anything touches the device.
+int somaopt::init_table(const somaopt_tensor_desc* descs, int64_t n_tensors, const somaopt_group* groups,
+                        int32_t n_groups, double max_norm, double grad_divisor, int64_t initial_step,
+                        void* stream, somaopt_handle** out, bool from_scratch) {
     if (!out) return fail(SOMAOPT_E_INVALID, "out is NULL");
     *out = nullptr;
     int rc = check_groups(groups, n_groups);
@@ -306,11 +359,6 @@ int somaopt_init_tensor_table(const somaopt_tensor_desc* descs, int64_t n_tensor
     Counts counts;
     rc = validate_host(descs, n_tensors, n_groups, err, &counts);
     if (rc) return fail(rc, err);
-    int dev = -1;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-    if ((rc = check_pointers(descs, n_tensors, dev))) return rc;
-
     const int64_t ch1 = normalise_chunk(env_int("SOMAOPT_PASS1_CHUNK", 0), kDefaultPass1Chunk);
     const int64_t ch2 = normalise_chunk(env_int("SOMAOPT_PASS2_CHUNK", 0), kDefaultPass2Chunk, kMaxPass2Chunk);
     const int64_t cost1 = std::max<int64_t>(0, env_int("SOMAOPT_SEGMENT_COST", kSegmentCost));
@@ -356,6 +404,38 @@ int somaopt_init_tensor_table(const somaopt_tensor_desc* descs, int64_t n_tensor
         s2[i].lowp_dtype = (uint8_t)(t.param_lowp ? t.lowp_dtype : 0);
     }
 
+    // Device bytes of the table build (the order of place_buffers below).
+    const uint32_t nblk1 = (uint32_t)(p1.block_first.size() - 1);
+    auto place_buffers = [&](somaopt_handle* hh, Placer& where, hipStream_t s,
+                             const std::vector<DevState>& stv) -> hipError_t {
+        hipError_t e;
+        if ((e = alloc_upload(&hh->d_seg1, s1, s, where)) != hipSuccess ||
+            (e = alloc_upload(&hh->d_blk1, p1.block_first, s, where)) != hipSuccess ||
+            (e = alloc_upload(&hh->d_seg2, s2, s, where)) != hipSuccess ||
+            (e = alloc_upload(&hh->d_blk2, p2.block_first, s, where)) != hipSuccess ||
+            (e = alloc_upload(&hh->d_state, stv, s, where)) != hipSuccess ||
+            (e = where.get(reinterpret_cast<void**>(&hh->d_partials),
+                           sizeof(double) * std::max<uint32_t>(nblk1, 1))) != hipSuccess ||
+            (e = where.get(reinterpret_cast<void**>(&hh->d_partials2),
+                           sizeof(double) * ((nblk1 + kReduceSpan - 1) / kReduceSpan + 1))) != hipSuccess)
+            return e;
+        return hipSuccess;
+    };
+    if (from_scratch) {
+        somaopt_handle probe;
+        Placer count;
+        count.counting = true;
+        (void)place_buffers(&probe, count, nullptr, std::vector<DevState>(1));
+        if (count.used > scratch_capacity())
+            return fail(SOMAOPT_E_INVALID, "the table needs " + std::to_string(count.used) +
+                                               " bytes of device scratch; the no-allocation entry point holds at most " +
+                                               std::to_string(scratch_capacity()) + " (use somaopt_init_tensor_table)");
+    }
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if ((rc = check_pointers(descs, n_tensors, dev))) return rc;
+
     DevState st;
     std::memset(&st, 0, sizeof(st));
     st.n_groups = n_groups;
@@ -393,31 +473,35 @@ int somaopt_init_tensor_table(const somaopt_tensor_desc* descs, int64_t n_tensor
     if (slice >= 0) h->info.pass2_launches = update_launches(h->nblk2, slice);
     hipStream_t s = static_cast<hipStream_t>(stream);
 
-    if ((e = alloc_upload(&h->d_seg1, s1, s)) != hipSuccess ||
-        (e = alloc_upload(&h->d_blk1, p1.block_first, s)) != hipSuccess ||
-        (e = alloc_upload(&h->d_seg2, s2, s)) != hipSuccess ||
-        (e = alloc_upload(&h->d_blk2, p2.block_first, s)) != hipSuccess) {
+    Placer where;
+    if (from_scratch) {
+        if ((rc = scratch_base(dev, &where.region)) != SOMAOPT_OK) {
+            free_handle(h);
+            return rc;
+        }
+        // From here on the scratch array is overwritten: every handle built
+        // on it earlier is superseded.
+        h->scratch = true;
+        h->scratch_gen = scratch_claim(dev);
+    }
+    // The whole state block is uploaded (every field that must start at zero
+    // is zero in it); the partials are written by each norm pass before they
+    // are read, so they need no clearing.
+    const std::vector<DevState> stv(1, st);
+    if ((e = place_buffers(h, where, s, stv)) != hipSuccess || (e = hipStreamSynchronize(s)) != hipSuccess) {
         free_handle(h);
         return e == hipErrorOutOfMemory ? fail(SOMAOPT_E_NOMEM, "device allocation of the tables failed")
                                         : hip_fail(e, "table upload");
-    }
-    std::vector<DevState> stv(1, st);
-    if ((e = alloc_upload(&h->d_state, stv, s)) != hipSuccess ||
-        (e = hipMalloc(reinterpret_cast<void**>(&h->d_partials), sizeof(double) * std::max<uint32_t>(h->nblk1, 1))) !=
-            hipSuccess ||
-        (e = hipMalloc(reinterpret_cast<void**>(&h->d_partials2),
-                       sizeof(double) * ((h->nblk1 + kReduceSpan - 1) / kReduceSpan + 1))) != hipSuccess ||
-        (e = hipStreamSynchronize(s)) != hipSuccess) {
-        free_handle(h);
-        return e == hipErrorOutOfMemory ? fail(SOMAOPT_E_NOMEM, "device allocation failed")
-                                        : hip_fail(e, "state upload");
     }
     *out = h;
     return SOMAOPT_OK;
 }
 
+extern "C" {
+
+
 int somaopt_grad_sqnorm(somaopt_handle* h, void* stream) {
-    if (!h) return fail(SOMAOPT_E_INVALID, "handle is NULL");
+    if (int bad = check_handle(h)) return bad;
     DeviceGuard g(h->device);
     if (!g.ok()) return fail(SOMAOPT_E_HIP, "cannot select the handle's device");
     int rc = launch_norm_pass(h, h->pending ? 0 : 1, static_cast<hipStream_t>(stream));
@@ -427,7 +511,7 @@ int somaopt_grad_sqnorm(somaopt_handle* h, void* stream) {
 }
 
 int somaopt_fused_adamw_step(somaopt_handle* h, void* stream) {
-    if (!h) return fail(SOMAOPT_E_INVALID, "handle is NULL");
+    if (int bad = check_handle(h)) return bad;
     if (!h->pending) return fail(SOMAOPT_E_STATE, "somaopt_grad_sqnorm must precede each update");
     DeviceGuard g(h->device);
     if (!g.ok()) return fail(SOMAOPT_E_HIP, "cannot select the handle's device");
@@ -438,7 +522,7 @@ int somaopt_fused_adamw_step(somaopt_handle* h, void* stream) {
 }
 
 int somaopt_register_arrival(somaopt_handle* h, const void* const* incoming, int64_t n_tensors, void* stream) {
-    if (!h) return fail(SOMAOPT_E_INVALID, "handle is NULL");
+    if (int bad = check_handle(h)) return bad;
     if (h->d_seg3) return fail(SOMAOPT_E_STATE, "arriving buffers are already registered for this handle");
     if (n_tensors != (int64_t)h->descs.size())
         return fail(SOMAOPT_E_INVALID, "n_tensors differs from the table given at init");
@@ -500,7 +584,7 @@ int somaopt_register_arrival(somaopt_handle* h, const void* const* incoming, int
 }
 
 int somaopt_arrival_sqnorm(somaopt_handle* h, int32_t accumulate, void* stream) {
-    if (!h) return fail(SOMAOPT_E_INVALID, "handle is NULL");
+    if (int bad = check_handle(h)) return bad;
     if (!h->d_seg3) return fail(SOMAOPT_E_STATE, "somaopt_register_arrival must precede the arrival pass");
     if (accumulate != 0 && accumulate != 1) return fail(SOMAOPT_E_INVALID, "accumulate must be 0 or 1");
     DeviceGuard g(h->device);
@@ -512,7 +596,7 @@ int somaopt_arrival_sqnorm(somaopt_handle* h, int32_t accumulate, void* stream) 
 }
 
 int somaopt_set_groups(somaopt_handle* h, const somaopt_group* groups, int32_t n_groups, void* stream) {
-    if (!h) return fail(SOMAOPT_E_INVALID, "handle is NULL");
+    if (int bad = check_handle(h)) return bad;
     if (n_groups != h->n_groups) return fail(SOMAOPT_E_INVALID, "n_groups differs from the handle's");
     int rc = check_groups(groups, n_groups);
     if (rc) return rc;
@@ -527,7 +611,7 @@ int somaopt_set_groups(somaopt_handle* h, const somaopt_group* groups, int32_t n
 }
 
 int somaopt_set_schedules(somaopt_handle* h, const somaopt_schedule* schedules, int32_t n_groups, void* stream) {
-    if (!h) return fail(SOMAOPT_E_INVALID, "handle is NULL");
+    if (int bad = check_handle(h)) return bad;
     if (n_groups != h->n_groups) return fail(SOMAOPT_E_INVALID, "n_groups differs from the handle's");
     if (!schedules) return fail(SOMAOPT_E_INVALID, "schedules is NULL");
     ScheduleArgs a;
@@ -557,7 +641,7 @@ int somaopt_set_schedules(somaopt_handle* h, const somaopt_schedule* schedules, 
 }
 
 int somaopt_set_clip(somaopt_handle* h, double max_norm, double grad_divisor, void* stream) {
-    if (!h) return fail(SOMAOPT_E_INVALID, "handle is NULL");
+    if (int bad = check_handle(h)) return bad;
     int rc = check_clip(max_norm, grad_divisor);
     if (rc) return rc;
     DeviceGuard g(h->device);
@@ -567,7 +651,7 @@ int somaopt_set_clip(somaopt_handle* h, double max_norm, double grad_divisor, vo
 }
 
 int somaopt_set_step(somaopt_handle* h, int64_t step, void* stream) {
-    if (!h) return fail(SOMAOPT_E_INVALID, "handle is NULL");
+    if (int bad = check_handle(h)) return bad;
     if (step < 0) return fail(SOMAOPT_E_INVALID, "step < 0");
     DeviceGuard g(h->device);
     if (!g.ok()) return fail(SOMAOPT_E_HIP, "cannot select the handle's device");
@@ -637,19 +721,19 @@ int capture(somaopt_handle* h, int arrival) {
 extern "C" {
 
 int somaopt_capture_step(somaopt_handle* h) {
-    if (!h) return fail(SOMAOPT_E_INVALID, "handle is NULL");
+    if (int bad = check_handle(h)) return bad;
     return capture(h, -1);
 }
 
 int somaopt_capture_arrival_step(somaopt_handle* h, int32_t accumulate) {
-    if (!h) return fail(SOMAOPT_E_INVALID, "handle is NULL");
+    if (int bad = check_handle(h)) return bad;
     if (!h->d_seg3) return fail(SOMAOPT_E_STATE, "somaopt_register_arrival must precede the capture");
     if (accumulate != 0 && accumulate != 1) return fail(SOMAOPT_E_INVALID, "accumulate must be 0 or 1");
     return capture(h, accumulate);
 }
 
 int somaopt_replay_step(somaopt_handle* h, void* stream) {
-    if (!h) return fail(SOMAOPT_E_INVALID, "handle is NULL");
+    if (int bad = check_handle(h)) return bad;
     if (!h->exec) return fail(SOMAOPT_E_STATE, "no captured step (call somaopt_capture_step)");
     if (h->pending) return fail(SOMAOPT_E_STATE, "an eager norm or arrival pass is pending; finish it with somaopt_fused_adamw_step");
     DeviceGuard g(h->device);
@@ -660,12 +744,14 @@ int somaopt_replay_step(somaopt_handle* h, void* stream) {
 
 int somaopt_device_stats(somaopt_handle* h, const void** stats_dev) {
     if (!h || !stats_dev) return fail(SOMAOPT_E_INVALID, "NULL argument");
+    if (int bad = check_handle(h)) return bad;
     *stats_dev = &h->d_state->stats;
     return SOMAOPT_OK;
 }
 
 int somaopt_read_stats(somaopt_handle* h, somaopt_stats* out, int64_t* steps_out, void* stream) {
     if (!h || !out) return fail(SOMAOPT_E_INVALID, "NULL argument");
+    if (int bad = check_handle(h)) return bad;
     DeviceGuard g(h->device);
     if (!g.ok()) return fail(SOMAOPT_E_HIP, "cannot select the handle's device");
     hipStream_t s = static_cast<hipStream_t>(stream);

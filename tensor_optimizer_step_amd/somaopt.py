@@ -90,6 +90,10 @@ SIGNATURES = {
                                                  ctypes.POINTER(Group), ctypes.c_int32,
                                                  ctypes.c_double, ctypes.c_double, ctypes.c_int64,
                                                  _P, _PP]),
+    "somaopt_init_tensor_table_noalloc": (ctypes.c_int, [ctypes.POINTER(TensorDesc), ctypes.c_int64,
+                                                         ctypes.POINTER(Group), ctypes.c_int32,
+                                                         ctypes.c_double, ctypes.c_double, ctypes.c_int64,
+                                                         _P, _PP]),
     "somaopt_grad_sqnorm": (ctypes.c_int, [_P, _P]),
     "somaopt_fused_adamw_step": (ctypes.c_int, [_P, _P]),
     "somaopt_set_groups": (ctypes.c_int, [_P, ctypes.POINTER(Group), ctypes.c_int32, _P]),
@@ -274,14 +278,17 @@ class FusedAdamW:
     ``grads`` fp32, bf16 or fp16 CUDA tensors (entries of frozen tensors may be
     None).  ``params_lowp`` optionally gives a bf16/fp16 working copy per
     tensor (None entries: no copy).  The tensors must stay alive and in place
-    while the handle lives.
+    while the handle lives.  ``noalloc`` builds the handle with
+    somaopt_init_tensor_table_noalloc (its device tables in the library's
+    per-device scratch array, no device allocation; a later such handle on the
+    same device supersedes it).
     """
 
     def __init__(self, params: Sequence, grads: Sequence, exp_avgs: Sequence,
                  exp_avg_sqs: Sequence, group_of: Sequence[int], groups: Sequence,
                  max_norm: float, grad_divisor: float, trainable: Optional[Sequence[bool]] = None,
                  owner: Optional[Sequence[bool]] = None, initial_step: int = 0, stream=None,
-                 params_lowp: Optional[Sequence] = None):
+                 params_lowp: Optional[Sequence] = None, noalloc: bool = False):
         self._lib = load()
         n = len(params)
         trainable = [True] * n if trainable is None else list(trainable)
@@ -315,9 +322,9 @@ class FusedAdamW:
         self._groups = make_groups(groups)
         descs = make_descs(rows)
         h = ctypes.c_void_p()
-        _check(self._lib.somaopt_init_tensor_table(
-            descs, n, self._groups, self.n_groups, float(max_norm), float(grad_divisor),
-            int(initial_step), _stream_ptr(stream), ctypes.byref(h)))   # init waits for it
+        init = self._lib.somaopt_init_tensor_table_noalloc if noalloc else self._lib.somaopt_init_tensor_table
+        _check(init(descs, n, self._groups, self.n_groups, float(max_norm), float(grad_divisor),
+                    int(initial_step), _stream_ptr(stream), ctypes.byref(h)))   # init waits for it
         self._h = h
 
     def _s(self, stream) -> Optional[int]:

@@ -318,3 +318,18 @@ def test_bench_traffic_record_needs_same_kernel_and_split(tmp_path, monkeypatch)
     (tmp_path / "traffic_pass2_old.json").write_text(json.dumps(old))
     assert bench.load_traffic("old", 1) == 777
     assert bench.load_traffic("old", 2) is None
+
+
+def test_noalloc_init_refuses_tables_beyond_its_scratch():
+    """The no-allocation build counts its device bytes before touching any
+    device: a table that needs more than the 32 MiB scratch array is refused
+    with both sizes in the message (fake, never dereferenced addresses)."""
+    lib = S.load()
+    rows = [(1 << 40, 2 << 40, 3 << 40, 4 << 40, 1 << 31, S.F32, 0, 1, 1)]
+    descs = S.make_descs(rows)
+    groups = S.make_groups([dict(lr=1e-3, weight_decay=0.0, beta1=0.9, beta2=0.999, eps=1e-8)])
+    h = S.ctypes.c_void_p()
+    rc = lib.somaopt_init_tensor_table_noalloc(descs, 1, groups, 1, 1.0, 1.0, 0, None, S.ctypes.byref(h))
+    assert rc == S.E_INVALID and not h.value
+    msg = S.last_error()
+    assert "bytes of device scratch" in msg and "33554432" in msg, msg
