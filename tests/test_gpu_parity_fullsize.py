@@ -1,15 +1,22 @@
 """Full-size parity in the launch configuration the benchmark times.
 
-The whole step runs as the captured HIP graph with the default chunking.  The
-oracle follows every step on sampled elements (the update is elementwise, so a
-sample is exact) after computing each step's global norm from ALL owned
-gradients on the host.  Gradient buffers are checked unchanged on the device
-against a clone; frozen/untouched regions by bitwise comparison.
+The whole step runs as the captured HIP graph with the default chunking.
+Every step's global norm is computed by the oracle on the host from ALL owned
+gradients.  Element comparisons cover every element:
 
-Workloads: the 302,092,288-element action expert (10 steps), the
-6,738,939,904-element 7B backbone (10 steps, norm alternating 0.5x / 5x
-max_norm), and the same 7B state cut into four contiguous shards on one device
-with replicated, singly-owned RMSNorms (10 steps, cosine lr).
+* the 302,092,288-element action expert (arena layout): the oracle keeps the
+  fp64 state of every element of every tensor and all of p, m and v are
+  compared after 10 steps (the per-tensor layout and the working-copy run
+  follow sampled windows);
+* the 6,738,939,904-element 7B backbone and the same state cut into four
+  shards with replicated RMSNorms: after steps 1 and 2, every element of every
+  tensor (every piece and every replica) is compared with the oracle run on
+  that tensor alone from its regenerated seeded inputs and the steps' global
+  clip coefficients, streamed piece by piece; steps 3..10 follow sampled
+  windows.  This covers the update pass's split into 13 launches and the cuts
+  between shards element by element.
+
+Gradient buffers are checked unchanged on the device against a clone.
 """
 from concurrent.futures import ThreadPoolExecutor
 
@@ -64,6 +71,97 @@ def host_sumsq_by_tensor(grads_dev, divisor):
     return total
 
 
+PIECE = 1 << 22
+
+
+def host_sumsq(g_host, divisor):
+    """As host_sumsq_by_tensor, from host copies already taken."""
+    with ThreadPoolExecutor(WORKERS) as ex:
+        parts = list(ex.map(lambda x: O.normalized_sumsq([x], [True], divisor), g_host))
+    total = 0.0
+    for x in parts:
+        total += x
+    return total
+
+
+def _groups_at(wl, lrs):
+    return [O.Group(lr, h.weight_decay, h.beta1, h.beta2, h.eps) for lr, h in zip(lrs, wl.groups)]
+
+
+def stream_check(wl, k_done, coefs, lrs_per_step, locate, label):
+    """Every element of every trainable tensor after update k_done, against the
+    oracle run on that tensor alone: its seeded initial weights and gradients
+    are regenerated, the oracle applies updates 1..k_done with the global clip
+    coefficients ``coefs`` (from the full norm of each step) and the per-step
+    learning rates, and the result is compared with the device state, in
+    pieces of PIECE elements on a thread pool.  ``locate(i, a, b)`` returns the
+    device (p, m, v) views holding logical elements [a, b) of tensor i as a
+    list of (start, stop, p, m, v) covering the range (several when the range
+    crosses a shard cut; every replica of a replicated tensor is listed)."""
+    worst = [0.0, 0.0, 0.0]
+    n_checked = 0
+    with ThreadPoolExecutor(WORKERS) as ex:
+        for i, t in enumerate(wl.tensors):
+            if not t.trainable:
+                continue
+            p0 = W.param_values(wl, i, "cuda").cpu().numpy()
+            gs = [W.to_numpy_grad(W.grad_values(wl, i, k, "cuda")) for k in range(1, k_done + 1)]
+            grp = [_groups_at(wl, lrs_per_step[k])[t.group] for k in range(k_done)]
+
+            def piece(ab, i=i, p0=p0, gs=gs, grp=grp):
+                a, b = ab
+                p = np.asarray(p0[a:b], np.float64)
+                m = np.zeros(b - a)
+                v = np.zeros(b - a)
+                for k in range(k_done):
+                    p, m, v = O.update_elements(p, m, v, gs[k][a:b], coefs[k], wl.grad_divisor, grp[k], k + 1)
+                out = [0.0, 0.0, 0.0]
+                for lo, hi, dp, dm, dv in locate(i, a, b):
+                    for j, (dt, want) in enumerate(((dp, p), (dm, m), (dv, v))):
+                        got = dt.cpu().numpy()
+                        out[j] = max(out[j], assert_close(f"{label} step {k_done} {'pmv'[j]}[{i}][{lo}:{hi}]",
+                                                          got, want[lo - a:hi - a]))
+                return out
+
+            for r in ex.map(piece, [(a, min(a + PIECE, t.numel)) for a in range(0, t.numel, PIECE)]):
+                worst = [max(x, y) for x, y in zip(worst, r)]
+            n_checked += t.numel
+            if i % 40 == 0:
+                log(f"[fullsize] {label}: step {k_done} checked through tensor {i} ({n_checked} elements)")
+    log(f"[fullsize] {label}: every element after step {k_done} ({n_checked} per kind) within the bar; "
+        f"tensor-wise rel err p={worst[0]:.2e} m={worst[1]:.2e} v={worst[2]:.2e}")
+
+
+class FullOracle:
+    """fp64 oracle state for every element of every trainable tensor, updated
+    in pieces on a thread pool (the update is elementwise)."""
+
+    def __init__(self, wl, p0_host):
+        self.wl = wl
+        self.p = [np.asarray(x, np.float64) for x in p0_host]
+        self.m = [np.zeros_like(x) for x in self.p]
+        self.v = [np.zeros_like(x) for x in self.p]
+        self.t = [0] * len(wl.groups)
+
+    def step(self, g_host, sumsq, lrs):
+        norm = float(np.sqrt(sumsq))
+        coef = O.clip_coefficient(norm, self.wl.max_norm)
+        for k in range(len(self.t)):
+            self.t[k] += 1
+        groups = _groups_at(self.wl, lrs)
+        jobs = [(i, a, min(a + PIECE, t.numel)) for i, t in enumerate(self.wl.tensors) for a in range(0, t.numel, PIECE)]
+
+        def piece(job):
+            i, a, b = job
+            k = self.wl.tensors[i].group
+            self.p[i][a:b], self.m[i][a:b], self.v[i][a:b] = O.update_elements(
+                self.p[i][a:b], self.m[i][a:b], self.v[i][a:b], g_host[i][a:b], coef, self.wl.grad_divisor,
+                groups[k], self.t[k])
+        with ThreadPoolExecutor(WORKERS) as ex:
+            list(ex.map(piece, jobs))
+        return norm, coef
+
+
 class SampledOracle:
     """fp64 oracle state for sampled elements of every trainable tensor."""
 
@@ -94,13 +192,19 @@ def _gather(t, idx):
     return t[torch.as_tensor(idx, device=t.device)].cpu()
 
 
-@pytest.mark.parametrize("layout", ["arena", "tensor"])
-def test_action_expert_full_size_sampled(layout):
-    run_unsharded(W.action_expert(), layout=layout)
+def test_action_expert_full_size_every_element():
+    """Arena layout (the bench's): the oracle follows every element and all of
+    p, m and v are compared after 10 steps."""
+    run_unsharded(W.action_expert(), layout="arena", full=True)
 
 
-def test_backbone_7b_full_size_sampled():
-    run_unsharded(W.backbone_7b())
+def test_action_expert_full_size_tensor_layout_sampled():
+    run_unsharded(W.action_expert(), layout="tensor")
+
+
+def test_backbone_7b_full_size():
+    """Every element after steps 1 and 2 (streamed), sampled windows to 10."""
+    run_unsharded(W.backbone_7b(), stream_after=(1, 2))
 
 
 def test_action_expert_full_size_bf16_working_copy():
@@ -140,31 +244,46 @@ def _state(wl, dev, layout, lowp):
     return views[0], views[1], views[2], views[3], (views[4] if lowp is not None else None)
 
 
-def run_unsharded(wl, lowp=None, layout="arena"):
+def run_unsharded(wl, lowp=None, layout="arena", full=False, stream_after=()):
+    """``full``: the oracle follows every element and every element is compared
+    at the end; else sampled windows, plus a streamed every-element check after
+    each step in ``stream_after``."""
     from tensor_optimizer_step_amd.somaopt import FusedAdamW
     log(f"[fullsize] {wl.name}: {wl.n_tensors} tensors, {wl.trainable_numel} elements, {layout} layout")
     rng = np.random.default_rng(7)
     dev = "cuda"
     p, g, m, v, lp = _state(wl, dev, layout, lowp)
     idx = [sample_indices(t.numel, rng) for t in wl.tensors]
-    ora = SampledOracle(wl, [_gather(x, ix).numpy() for x, ix in zip(p, idx)], idx)
+    if full:
+        ora = FullOracle(wl, [x.cpu().numpy() for x in p])
+    else:
+        ora = SampledOracle(wl, [_gather(x, ix).numpy() for x, ix in zip(p, idx)], idx)
     opt = FusedAdamW(p, g, m, v, [t.group for t in wl.tensors], wl.groups, wl.max_norm,
                      wl.grad_divisor, params_lowp=lp)
     opt.capture()
     sumsq_cache = {}
+    coefs, lrs_hist = [], []
     for k in range(1, wl.steps + 1):
         for i in range(wl.n_tensors):
             g[i].copy_(W.grad_values(wl, i, k, dev))
         key = k if not wl.grad_period else (1 + (k - 1) % wl.grad_period, wl.grad_std(k))
+        g_host = [W.to_numpy_grad(x) for x in g] if full else None
         if key not in sumsq_cache:
-            sumsq_cache[key] = host_sumsq_by_tensor(g, wl.grad_divisor)
+            sumsq_cache[key] = (host_sumsq(g_host, wl.grad_divisor) if full
+                                else host_sumsq_by_tensor(g, wl.grad_divisor))
         g_clone = [x.clone() for x in g] if k in (1, wl.steps) else None
         lrs = wl.lrs_for_step(k)
         opt.set_lrs(lrs)
         opt.replay()
         stats, steps = opt.read_stats()
-        g_s = [W.to_numpy_grad(_gather(x, ix)) for x, ix in zip(g, idx)]
-        norm, coef = ora.step(g_s, sumsq_cache[key], lrs)
+        if full:
+            norm, coef = ora.step(g_host, sumsq_cache[key], lrs)
+            del g_host
+        else:
+            g_s = [W.to_numpy_grad(_gather(x, ix)) for x, ix in zip(g, idx)]
+            norm, coef = ora.step(g_s, sumsq_cache[key], lrs)
+        coefs.append(coef)
+        lrs_hist.append(lrs)
         assert_norm(stats.norm, norm)
         assert stats.clip_coef == pytest.approx(coef, rel=1e-12)
         assert steps == [k] * len(wl.groups)
@@ -172,11 +291,28 @@ def run_unsharded(wl, lowp=None, layout="arena"):
             assert all(torch.equal(a, b) for a, b in zip(g, g_clone)), "a gradient buffer changed"
             del g_clone
         log(f"[fullsize] {wl.name} step {k}: norm {stats.norm:.6g} coef {stats.clip_coef:.6g}")
+        if k in stream_after:
+            torch.cuda.synchronize()
+            stream_check(wl, k, coefs, lrs_hist, lambda i, a, b: [(a, b, p[i][a:b], m[i][a:b], v[i][a:b])],
+                         wl.name)
     torch.cuda.synchronize()
     worst = [0.0, 0.0, 0.0]
-    for i in range(wl.n_tensors):
-        for j, (dev_t, want) in enumerate(((p[i], ora.p[i]), (m[i], ora.m[i]), (v[i], ora.v[i]))):
-            worst[j] = max(worst[j], assert_close(f"{'pmv'[j]}[{i}]", _gather(dev_t, idx[i]).numpy(), want))
+    if full:
+        jobs = [(i, a, min(a + PIECE, t.numel)) for i, t in enumerate(wl.tensors) for a in range(0, t.numel, PIECE)]
+
+        def piece(job):
+            i, a, b = job
+            return [assert_close(f"{'pmv'[j]}[{i}][{a}:{b}]", dev_t[a:b].cpu().numpy(), want[a:b])
+                    for j, (dev_t, want) in enumerate(((p[i], ora.p[i]), (m[i], ora.m[i]), (v[i], ora.v[i])))]
+        with ThreadPoolExecutor(WORKERS) as ex:
+            for r in ex.map(piece, jobs):
+                worst = [max(x, y) for x, y in zip(worst, r)]
+        log(f"[fullsize] {wl.name}: every element of p, m, v after {wl.steps} steps within the bar "
+            f"({wl.trainable_numel} per kind)")
+    else:
+        for i in range(wl.n_tensors):
+            for j, (dev_t, want) in enumerate(((p[i], ora.p[i]), (m[i], ora.m[i]), (v[i], ora.v[i]))):
+                worst[j] = max(worst[j], assert_close(f"{'pmv'[j]}[{i}]", _gather(dev_t, idx[i]).numpy(), want))
     log(f"[fullsize] {wl.name}: tensor-wise rel err p={worst[0]:.2e} m={worst[1]:.2e} v={worst[2]:.2e}")
     if lp is not None:
         for i in range(wl.n_tensors):
@@ -186,10 +322,12 @@ def run_unsharded(wl, lowp=None, layout="arena"):
     del p, g, m, v, lp
 
 
-def test_sharded_7b_full_size_sampled():
+def test_sharded_7b_full_size():
     """Four contiguous shards of the 7B matrices plus four RMSNorm replicas
     (owner = shard 0), one handle of 488 descriptors; compared with the oracle
-    on the unsharded tensors, every replica included."""
+    on the unsharded tensors, every replica included: every element of every
+    piece and replica after steps 1 and 2 (streamed), sampled windows and the
+    neighbourhoods of the cuts to step 10."""
     from tensor_optimizer_step_amd.somaopt import FusedAdamW
     lay = W.sharded_7b()
     wl = lay.base
@@ -250,7 +388,21 @@ def test_sharded_7b_full_size_sampled():
     assert info.trainable_numel == wl.trainable_numel + (S - 1) * sum(
         t.numel for t in wl.tensors if t.group == 1)
     opt.capture()
+
+    def locate(i, a, b):
+        """Device views of logical elements [a, b) of tensor i: the pieces
+        covering them (a range may cross a shard cut) and every replica."""
+        out = []
+        for q in by_tensor[i]:
+            lo, hi = max(a, q.t_offset), min(b, q.t_offset + q.numel)
+            if lo < hi:
+                s0 = q.s_offset + (lo - q.t_offset)
+                sl = slice(s0, s0 + hi - lo)
+                out.append((lo, hi, sp[q.shard][sl], sm[q.shard][sl], sv[q.shard][sl]))
+        return out
+
     sumsq_cache = {}
+    coefs, lrs_hist = [], []
     for k in range(1, wl.steps + 1):
         gl = []
         for i in range(wl.n_tensors):
@@ -267,9 +419,14 @@ def test_sharded_7b_full_size_sampled():
         g_s = [W.to_numpy_grad(_gather(x, ix)) for x, ix in zip(gl, idx)]
         del gl
         norm, coef = ora.step(g_s, sumsq_cache[key], lrs)
+        coefs.append(coef)
+        lrs_hist.append(lrs)
         assert_norm(stats.norm, norm)
         assert stats.clip_coef == pytest.approx(coef, rel=1e-12)
         log(f"[fullsize] sharded_7b step {k}: norm {stats.norm:.6g} coef {stats.clip_coef:.6g}")
+        if k in (1, 2):
+            torch.cuda.synchronize()
+            stream_check(wl, k, coefs, lrs_hist, locate, "sharded_7b")
     torch.cuda.synchronize()
     for i, t in enumerate(wl.tensors):
         for j, (bufs, want) in enumerate(((sp, ora.p[i]), (sm, ora.m[i]), (sv, ora.v[i]))):
