@@ -140,23 +140,78 @@ __device__ __forceinline__ double block_sum(double x, double* lds) {
     return s;
 }
 
+// ------------------------------------------------- buffer-instruction access
+
+// Buffer resource over `bytes` bytes at `base` (raw addressing, stride 0):
+// the hardware bounds-checks every access against the segment, so a load past
+// the end returns zero and a store past it is dropped.  Word 3 selects the
+// 32-bit data format that untyped buffer accesses require on gfx9-family parts.
+constexpr int kRsrcWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t seg_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+// Cache-policy operand of the streaming buffer accesses: nt (nontemporal).
+// Every byte is used exactly once per step; on gfx950 the hint raises the
+// sustained bandwidth of this 4-read / 3-write stream by about a tenth over
+// plain accesses.
+constexpr int kLdPolicy = 2;
+constexpr int kStPolicy = 2;
+
+__device__ __forceinline__ f32x4 bload4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kLdPolicy));
+}
+__device__ __forceinline__ u32x2 bload2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kLdPolicy));
+}
+__device__ __forceinline__ void bstore4(__amdgpu_buffer_rsrc_t r, uint32_t off, const f32x4& x) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, (int)off, 0, kStPolicy);
+}
+__device__ __forceinline__ void bstore2(__amdgpu_buffer_rsrc_t r, uint32_t off, const u32x2& x) {
+    __builtin_amdgcn_raw_buffer_store_b64(x, r, (int)off, 0, kStPolicy);
+}
+
 // ------------------------------------------------------------------ pass 1
 
-// Sum of squares of one 16-bit-gradient segment (bf16 or fp16): 16-byte loads
-// of eight values, exact widening, fp64 accumulation.  The loop is unrolled
-// four times, so a thread issues all four loads of a full 8,192-element
-// segment at once (measured 6% faster than two at a time on MI355X).
-template <int BS, int DT>
-__device__ __forceinline__ void sumsq16(const Seg1& sg, int tid, double& a0, double& a1) {
-    const AS_GLOBAL uint16_t* g = gptr<uint16_t>(sg.g);
-    for (uint32_t k = tid; k < sg.head; k += BS) {
-        const double x = widen16<DT>(g[k]);
-        a0 = fma(x, x, a0);
-    }
-    const AS_GLOBAL u32x4* gv = (const AS_GLOBAL u32x4*)(g + sg.head);
-#pragma unroll 4
-    for (uint32_t i = tid; i < sg.nvec; i += BS) {
-        const u32x4 q = gv[i];
+// Sum of squares of one gradient segment: a scalar head (fewer elements than
+// a 16-byte vector), a body of 16-byte vectors and a scalar tail.  The body is
+// read through a buffer resource bounded by its own bytes, kPass1Batch vectors
+// per thread per round with every load of a round issued before the first
+// square (lanes past the end read zero, which adds an exact zero), so a short
+// segment costs one memory latency however many vectors per thread it has up
+// to kPass1Batch.  The head and tail elements are requested before the body
+// through a resource bounded by the whole segment and squared after it.
+constexpr int kPass1Batch = 4;
+// Cache policy of the norm pass's loads: the default one.  Nontemporal loads
+// here make the update pass that follows 6-7% slower on MI355X (measured in
+// one process on the action expert and the 7B state), although the norm pass
+// itself is no slower with them.
+constexpr int kNormLdPolicy = 0;
+// Descriptors fetched together by a workgroup of several segments (at most
+// 8 with the default packing cost; later ones are fetched one by one).
+constexpr int kPrefetchSegs = 8;
+constexpr uint32_t kOutOfRange = 0x7fffffffu;   // a buffer offset past every segment
+
+template <int DT>
+__device__ __forceinline__ double widen_elem(uint32_t raw) {
+    if constexpr (DT == SOMAOPT_F32) return __uint_as_float(raw);
+    else return widen16<DT>((uint16_t)raw);
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t bload_elem(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    if constexpr (DT == SOMAOPT_F32) return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kNormLdPolicy);
+    else return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, kNormLdPolicy);
+}
+
+template <int DT>
+__device__ __forceinline__ void square_vec(const u32x4& q, double& a0, double& a1) {
+    if constexpr (DT == SOMAOPT_F32) {
+        double x;
+        x = __uint_as_float(q.x); a0 = fma(x, x, a0);
+        x = __uint_as_float(q.y); a1 = fma(x, x, a1);
+        x = __uint_as_float(q.z); a0 = fma(x, x, a0);
+        x = __uint_as_float(q.w); a1 = fma(x, x, a1);
+    } else {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const double lo = widen_lo<DT>(q[k]);
@@ -165,39 +220,43 @@ __device__ __forceinline__ void sumsq16(const Seg1& sg, int tid, double& a0, dou
             a1 = fma(hi, hi, a1);
         }
     }
-    if ((uint32_t)tid < sg.tail) {
-        const double x = widen16<DT>(g[sg.head + 8 * (size_t)sg.nvec + tid]);
-        a1 = fma(x, x, a1);
+}
+
+template <int BS, int DT>
+__device__ __forceinline__ void segment_sumsq_t(const Seg1& sg, int tid, double& a0, double& a1) {
+    constexpr uint32_t esz = DT == SOMAOPT_F32 ? 4u : 2u;
+    const char* g = static_cast<const char*>(sg.g);
+    const uint32_t body = sg.head * esz;
+    const uint32_t tail0 = body + 16u * sg.nvec;
+    const __amdgpu_buffer_rsrc_t rs = seg_rsrc(g, tail0 + sg.tail * esz);
+    const __amdgpu_buffer_rsrc_t rv = seg_rsrc(g + body, 16u * sg.nvec);
+    // a head or a tail has fewer elements than a 16-byte vector: one per thread at most
+    const uint32_t hraw = bload_elem<DT>(rs, (uint32_t)tid < sg.head ? tid * esz : kOutOfRange);
+    const uint32_t traw = bload_elem<DT>(rs, (uint32_t)tid < sg.tail ? tail0 + tid * esz : kOutOfRange);
+    for (uint32_t base = 0; base < sg.nvec; base += kPass1Batch * BS) {
+        u32x4 q[kPass1Batch];
+#pragma unroll
+        for (int u = 0; u < kPass1Batch; ++u)
+            q[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 rv, (int)(16u * (base + u * BS + tid)), 0, kNormLdPolicy));
+        __builtin_amdgcn_sched_barrier(0);   // every load of the round before the first square
+#pragma unroll
+        for (int u = 0; u < kPass1Batch; ++u) square_vec<DT>(q[u], a0, a1);
     }
+    const double h = widen_elem<DT>(hraw);
+    const double t = widen_elem<DT>(traw);
+    a0 = fma(h, h, a0);
+    a1 = fma(t, t, a1);
 }
 
 template <int BS>
 __device__ __forceinline__ void segment_sumsq(const Seg1& sg, int tid, double& a0, double& a1) {
-    if (sg.dtype == SOMAOPT_BF16) {
-        sumsq16<BS, SOMAOPT_BF16>(sg, tid, a0, a1);
-    } else if (sg.dtype == SOMAOPT_F16) {
-        sumsq16<BS, SOMAOPT_F16>(sg, tid, a0, a1);
-    } else {
-        const AS_GLOBAL float* g = gptr<float>(sg.g);
-        for (uint32_t k = tid; k < sg.head; k += BS) {
-            const double x = g[k];
-            a0 = fma(x, x, a0);
-        }
-        const AS_GLOBAL f32x4* gv = (const AS_GLOBAL f32x4*)(g + sg.head);
-#pragma unroll 4
-        for (uint32_t i = tid; i < sg.nvec; i += BS) {
-            const f32x4 q = gv[i];
-            double x;
-            x = q.x; a0 = fma(x, x, a0);
-            x = q.y; a1 = fma(x, x, a1);
-            x = q.z; a0 = fma(x, x, a0);
-            x = q.w; a1 = fma(x, x, a1);
-        }
-        if ((uint32_t)tid < sg.tail) {
-            const double x = g[sg.head + 4 * (size_t)sg.nvec + tid];
-            a1 = fma(x, x, a1);
-        }
-    }
+    if (sg.dtype == SOMAOPT_BF16)
+        segment_sumsq_t<BS, SOMAOPT_BF16>(sg, tid, a0, a1);
+    else if (sg.dtype == SOMAOPT_F16)
+        segment_sumsq_t<BS, SOMAOPT_F16>(sg, tid, a0, a1);
+    else
+        segment_sumsq_t<BS, SOMAOPT_F32>(sg, tid, a0, a1);
 }
 
 // Statistics of the pending update, computed once in fp64 by one thread.
@@ -279,9 +338,21 @@ __global__ __launch_bounds__(BS) void sqnorm_pass1(Pass1Args a) {
     const uint32_t s0 = blk[b];
     const uint32_t s1 = blk[b + 1];
     double a0 = 0.0, a1 = 0.0;
-    for (uint32_t s = s0; s < s1; ++s) {
-        const Seg1 sg = cload(segs + s);
-        segment_sumsq<BS>(sg, tid, a0, a1);
+    if (s1 == s0 + 1) {
+        segment_sumsq<BS>(cload(segs + s0), tid, a0, a1);
+    } else if (s1 > s0) {
+        // Several short segments: every descriptor of the block is requested
+        // at once (scalar loads complete in any order, so a descriptor
+        // fetched per segment would cost one wait each), then the segments
+        // are read from registers.
+        const uint32_t ns = s1 - s0;
+        Seg1 d[kPrefetchSegs];
+#pragma unroll
+        for (int j = 0; j < kPrefetchSegs; ++j) d[j] = cload(segs + s0 + min((uint32_t)j, ns - 1));
+#pragma unroll
+        for (int j = 0; j < kPrefetchSegs; ++j)
+            if ((uint32_t)j < ns) segment_sumsq<BS>(d[j], tid, a0, a1);
+        for (uint32_t s = s0 + kPrefetchSegs; s < s1; ++s) segment_sumsq<BS>(cload(segs + s), tid, a0, a1);
     }
     const double part = block_sum<BS>(a0 + a1, lds);
     if (tid == 0) a.partials[b] = part;
@@ -382,34 +453,6 @@ __device__ __forceinline__ u32x2 narrow4(const f32x4& p) {
 }
 
 constexpr int kNoLowp = -1;
-
-// Buffer resource over `bytes` bytes at `base` (raw addressing, stride 0):
-// the hardware bounds-checks every access against the segment, so a load past
-// the end returns zero and a store past it is dropped.  Word 3 selects the
-// 32-bit data format that untyped buffer accesses require on gfx9-family parts.
-constexpr int kRsrcWord3 = 0x00020000;
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t seg_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
-}
-// Cache-policy operand of the streaming buffer accesses: nt (nontemporal).
-// Every byte is used exactly once per step; on gfx950 the hint raises the
-// sustained bandwidth of this 4-read / 3-write stream by about a tenth over
-// plain accesses.
-constexpr int kLdPolicy = 2;
-constexpr int kStPolicy = 2;
-
-__device__ __forceinline__ f32x4 bload4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kLdPolicy));
-}
-__device__ __forceinline__ u32x2 bload2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kLdPolicy));
-}
-__device__ __forceinline__ void bstore4(__amdgpu_buffer_rsrc_t r, uint32_t off, const f32x4& x) {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, (int)off, 0, kStPolicy);
-}
-__device__ __forceinline__ void bstore2(__amdgpu_buffer_rsrc_t r, uint32_t off, const u32x2& x) {
-    __builtin_amdgcn_raw_buffer_store_b64(x, r, (int)off, 0, kStPolicy);
-}
 
 template <int GDT>
 __device__ __forceinline__ f32x4 widen_g4_buf(__amdgpu_buffer_rsrc_t r, uint32_t i) {
