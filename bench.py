@@ -58,9 +58,9 @@ def parse():
                          "byte count and torch's own clip_grad_norm_ + AdamW(fused=True) on the "
                          "same shapes (fp32 gradients, which torch's AdamW requires)")
     ap.add_argument("--layout", choices=["arena", "tensor"], default="arena",
-                    help="unsharded workloads: one buffer per kind (p, g, m, v) with the tensors as "
-                         "consecutive views at 64-element boundaries (default), or one allocation "
-                         "per tensor and kind")
+                    help="unsharded workloads: per-kind buffers (p, g, m, v) of at most 2^30 elements "
+                         "with the tensors as consecutive views at 64-element boundaries (default), or "
+                         "one allocation per tensor and kind")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for HBM counter scaling)")
     return ap.parse_args()
@@ -412,20 +412,22 @@ def plain_setup(torch, somaopt, W, wl, dev, stream, lowp_dtype, layout="arena"):
     p, g, m, v = [], [], [], []
     if layout == "arena":
         # every tensor starts at a multiple of 64 elements (256 B of fp32), as
-        # flat-buffer optimizers align them; the gaps are never touched
-        align = 64
-        offs, total = [], 0
-        for t in wl.tensors:
-            offs.append(total)
-            total += (t.numel + align - 1) // align * align
+        # flat-buffer optimizers align them, in per-kind buffers of at most
+        # 2^30 elements allocated kind by kind (p, then g, m, v); the gaps are
+        # never touched
+        place, sizes = W.arena_layout(wl)
         gdt = {W.torch_dtype(t.grad_dtype) for t in wl.tensors}
         if len(gdt) != 1:
             raise SystemExit("--layout arena needs one gradient dtype")
-        arena = {"p": torch.empty(total, device=dev), "g": torch.empty(total, dtype=gdt.pop(), device=dev),
-                 "m": torch.zeros(total, device=dev), "v": torch.zeros(total, device=dev)}
+        gdt = gdt.pop()
+        arena = {"p": [torch.empty(n, device=dev) for n in sizes],
+                 "g": [torch.empty(n, dtype=gdt, device=dev) for n in sizes],
+                 "m": [torch.zeros(n, device=dev) for n in sizes],
+                 "v": [torch.zeros(n, device=dev) for n in sizes]}
         for i, t in enumerate(wl.tensors):
+            c, o = place[i]
             for k, lst in zip("pgmv", (p, g, m, v)):
-                lst.append(arena[k][offs[i]:offs[i] + t.numel])
+                lst.append(arena[k][c][o:o + t.numel])
             p[-1].copy_(W.param_values(wl, i, dev))
             g[-1].copy_(W.grad_values(wl, i, 1, dev))
     else:
@@ -438,8 +440,8 @@ def plain_setup(torch, somaopt, W, wl, dev, stream, lowp_dtype, layout="arena"):
     if lowp_dtype != "none":
         ldt = W.torch_dtype(lowp_dtype)
         if layout == "arena":
-            lbuf = torch.empty(total, dtype=ldt, device=dev)
-            lowp = [lbuf[offs[i]:offs[i] + t.numel] for i, t in enumerate(wl.tensors)]
+            lbuf = [torch.empty(n, dtype=ldt, device=dev) for n in sizes]
+            lowp = [lbuf[c][o:o + t.numel] for (c, o), t in zip(place, wl.tensors)]
         else:
             lowp = [torch.empty(t.numel, dtype=ldt, device=dev) for t in wl.tensors]
     opt = somaopt.FusedAdamW(p, g, m, v, [t.group for t in wl.tensors], wl.groups, wl.max_norm,

@@ -292,6 +292,26 @@ def sharded_7b(n_shards: int = 4, **backbone_kw) -> ShardLayout:
                        shard_numel=[per + norm_numel] * n_shards, pieces=out)
 
 
+# Elements per buffer of the per-kind arena layout (4 GiB of fp32).
+ARENA_CHUNK = 1 << 30
+
+
+def arena_layout(wl: Workload, align: int = 64, max_elems: int = ARENA_CHUNK):
+    """Placement of every tensor in per-kind buffers (one set of buffers for
+    each of p, g, m, v): tensors in table order, each starting at a multiple of
+    ``align`` elements, a new buffer whenever the current one would pass
+    ``max_elems``.  Returns ([(buffer, offset)] per tensor, [elements per
+    buffer]); every kind uses the same placement."""
+    place, sizes = [], [0]
+    for t in wl.tensors:
+        n = -(-t.numel // align) * align
+        if sizes[-1] > 0 and sizes[-1] + n > max_elems:
+            sizes.append(0)
+        place.append((len(sizes) - 1, sizes[-1]))
+        sizes[-1] += n
+    return place, sizes
+
+
 WORKLOADS: dict = {
     "tiny": tiny,
     "action_expert": action_expert,

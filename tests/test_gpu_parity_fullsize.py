@@ -217,8 +217,8 @@ def test_action_expert_full_size_bf16_working_copy():
 
 def _state(wl, dev, layout, lowp):
     """The bench's layouts: "arena" holds each kind (p, g, m, v, working copy)
-    in one buffer with every tensor at a 64-element boundary; "tensor" makes
-    one allocation per tensor and kind."""
+    in buffers of at most 2^30 elements with every tensor at a 64-element
+    boundary; "tensor" makes one allocation per tensor and kind."""
     if layout == "tensor":
         p, g, m, v = [], [], [], []
         for i, t in enumerate(wl.tensors):
@@ -228,16 +228,13 @@ def _state(wl, dev, layout, lowp):
             v.append(torch.zeros(t.numel, device=dev))
         lp = [torch.empty(t.numel, dtype=lowp, device=dev) for t in wl.tensors] if lowp is not None else None
         return p, g, m, v, lp
-    offs, total = [], 0
-    for t in wl.tensors:
-        offs.append(total)
-        total += -(-t.numel // 64) * 64
+    place, sizes = W.arena_layout(wl)
     gdt = W.torch_dtype(wl.tensors[0].grad_dtype)
-    bufs = [torch.empty(total, device=dev), torch.empty(total, dtype=gdt, device=dev),
-            torch.zeros(total, device=dev), torch.zeros(total, device=dev)]
+    bufs = [[torch.empty(n, device=dev) for n in sizes], [torch.empty(n, dtype=gdt, device=dev) for n in sizes],
+            [torch.zeros(n, device=dev) for n in sizes], [torch.zeros(n, device=dev) for n in sizes]]
     if lowp is not None:
-        bufs.append(torch.empty(total, dtype=lowp, device=dev))
-    views = [[b[o:o + t.numel] for o, t in zip(offs, wl.tensors)] for b in bufs]
+        bufs.append([torch.empty(n, dtype=lowp, device=dev) for n in sizes])
+    views = [[b[c][o:o + t.numel] for (c, o), t in zip(place, wl.tensors)] for b in bufs]
     for i in range(wl.n_tensors):
         views[0][i].copy_(W.param_values(wl, i, dev))
         views[1][i].copy_(W.grad_values(wl, i, 1, dev))

@@ -123,3 +123,23 @@ def test_values_are_seeded():
     assert g.dtype == torch.bfloat16
     bits = W.to_numpy_grad(g)
     assert bits.dtype == np.uint16
+
+
+def test_arena_layout_places_every_tensor_once_aligned_and_bounded():
+    from tensor_optimizer_step_amd.workloads import arena_layout
+    for wl in (W.backbone_7b(layers=3, d=256, mlp=640, vocab=1000), W.launch_bound(n_tensors=500), W.tiny()):
+        for cap in (1 << 12, 1 << 16, 1 << 30):
+            place, sizes = arena_layout(wl, max_elems=cap)
+            assert len(place) == wl.n_tensors
+            spans = {}
+            for (c, o), t in zip(place, wl.tensors):
+                assert o % 64 == 0 and 0 <= c < len(sizes)
+                assert o + t.numel <= sizes[c]
+                spans.setdefault(c, []).append((o, o + t.numel))
+            for c, sp in spans.items():
+                sp.sort()
+                assert all(a[1] <= b[0] for a, b in zip(sp, sp[1:])), "tensors overlap"
+                # a buffer passes the cap only when one tensor alone does
+                assert sizes[c] <= cap or len(sp) == 1
+            # table order is kept: buffers and offsets never go backwards
+            assert all(p <= q for p, q in zip(place, place[1:]))
