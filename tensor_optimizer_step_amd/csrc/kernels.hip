@@ -23,6 +23,7 @@
 // partials from the new values in the same sweep, so the norm needs no second
 // read of the gradients.
 #include <hip/hip_runtime.h>
+#include <algorithm>
 
 #include "kernels.hpp"
 
@@ -773,10 +774,19 @@ hipError_t launch_reduce_finalize(const Pass1Args& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_pass3(const Pass3Args& a, hipStream_t s) {
-    hipLaunchKernelGGL(arrival_pass<kPass1Threads>, dim3(a.n_blocks), dim3(kPass1Threads), a.lds_bytes, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+hipError_t launch_pass3(const Pass3Args& a, uint32_t per_launch, hipStream_t s) {
+    const uint32_t per = per_launch == 0 ? a.n_blocks : per_launch;
+    for (uint32_t first = 0; first < a.n_blocks; first += per) {
+        // workgroups [first, first + n) read blk_first[first .. first + n]
+        // and write partials[first .. first + n)
+        Pass3Args x = a;
+        x.blk_first = a.blk_first + first;
+        x.partials = a.partials + first;
+        x.n_blocks = std::min(per, a.n_blocks - first);
+        hipLaunchKernelGGL(arrival_pass<kPass1Threads>, dim3(x.n_blocks), dim3(kPass1Threads), x.lds_bytes, s, x);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     Pass1Args r;
     r.segs = nullptr;
     r.blk_first = nullptr;

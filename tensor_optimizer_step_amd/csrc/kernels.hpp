@@ -40,6 +40,12 @@ constexpr int kPass2WgPerCuPacked = 4;
 // boundary costs about 4 us of ramp-down and ramp-up); a 302M-element table
 // (73,780 workgroups) is unchanged by splitting, so it stays one launch.
 constexpr uint32_t kPass2SliceBlocks = 131072;
+// Workgroups per arrival-pass launch (8,192 elements each), for the same
+// reason: the arrival pass reads and writes like the update pass.  Measured
+// on MI355X, 6.7e9 bf16 gradients accumulated (822K workgroups): 7.01 ms in
+// one launch, 6.86 at 131072 per launch, 6.81 at 65536, 6.78 at 32768; the
+// 302M-element table (36,890 workgroups) stays one launch.
+constexpr uint32_t kPass3SliceBlocks = 65536;
 // Number of launches for `n_blocks` workgroups at `per_launch` per launch
 // (0: one launch); every launch gets the same count, the last possibly fewer.
 inline int64_t update_launches(int64_t n_blocks, int64_t per_launch) {
@@ -102,7 +108,10 @@ struct Pass2Args {
 
 hipError_t launch_pass1(const Pass1Args& a, hipStream_t s);
 hipError_t launch_pass2(const Pass2Args& a, hipStream_t s);
-hipError_t launch_pass3(const Pass3Args& a, hipStream_t s);
+// The arrival pass as ceil(n_blocks / per_launch) launches over consecutive
+// ranges of its workgroups (per_launch 0: one launch), then the reduction of
+// all n_blocks partials.
+hipError_t launch_pass3(const Pass3Args& a, uint32_t per_launch, hipStream_t s);
 hipError_t launch_set_groups(DevState* st, const GroupArgs& g, hipStream_t s);
 hipError_t launch_set_schedules(DevState* st, const ScheduleArgs& a, hipStream_t s);
 hipError_t launch_set_clip(DevState* st, double max_norm, double grad_divisor, hipStream_t s);

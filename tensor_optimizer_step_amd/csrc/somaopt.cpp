@@ -47,6 +47,7 @@ struct somaopt_handle {
     uint32_t* d_blk3 = nullptr;
     uint32_t nblk3 = 0;
     uint32_t lds3 = 0;
+    uint32_t per3 = 0;             // arrival-pass workgroups per launch (0: one launch)
     double* d_partials3 = nullptr;
     double* d_partials3b = nullptr;
     int64_t pass1_chunk = 0;
@@ -580,6 +581,8 @@ int somaopt_register_arrival(somaopt_handle* h, const void* const* incoming, int
         hipSuccess)
         lds_per_cu = 0;
     h->lds3 = occupancy_lds(lds_per_cu, streaming_plan(p3) ? kPass1WgPerCuStreaming : 0);
+    const int64_t slice = env_int("SOMAOPT_PASS3_SLICE_BLOCKS", -1);
+    h->per3 = slice >= 0 ? (uint32_t)std::min<int64_t>(slice, 0xFFFFFFFFll) : kPass3SliceBlocks;
     return SOMAOPT_OK;
 }
 
@@ -678,7 +681,7 @@ int launch_arrival_pass(somaopt_handle* h, int advance, int32_t accumulate, hipS
     a.advance = advance;
     a.accumulate = accumulate;
     a.lds_bytes = h->lds3;
-    hipError_t e = launch_pass3(a, s);
+    hipError_t e = launch_pass3(a, h->per3, s);
     return e == hipSuccess ? SOMAOPT_OK : hip_fail(e, "arrival pass launch");
 }
 

@@ -212,14 +212,16 @@ def test_arrival_scaled_action_expert_many_workgroups():
     opt.close()
 
 
-@pytest.mark.parametrize("per_launch", [None, 5], ids=["one-update-launch", "split-update"])
+@pytest.mark.parametrize("per_launch", [None, 5], ids=["one-launch-each", "split-passes"])
 def test_arrival_graph_replay_equals_eager_bitwise(per_launch, monkeypatch):
     """{arrival, update} captured once and replayed equals the eager calls bit
     for bit, on two identical states; every replay is checked (several replays
-    with host synchronization between them).  With `per_launch` the update
-    pass goes out as several launches inside the captured step."""
+    with host synchronization between them).  With `per_launch` the arrival
+    and update passes each go out as several launches inside the captured
+    step."""
     if per_launch is not None:
         monkeypatch.setenv("SOMAOPT_PASS2_SLICE_BLOCKS", str(per_launch))
+        monkeypatch.setenv("SOMAOPT_PASS3_SLICE_BLOCKS", str(per_launch))
     wl = _workload([W.BF16, W.F32], seed_offset=31, n=30)
     states, opts, incs = [], [], []
     for graph in (False, True):
@@ -250,5 +252,47 @@ def test_arrival_graph_replay_equals_eager_bitwise(per_launch, monkeypatch):
         for name in "pgmv":
             for a, b in zip(getattr(states[0], name), getattr(states[1], name)):
                 assert np.array_equal(_bits(host(a)), _bits(host(b))), f"replay {k}: {name} differs"
+    for o in opts:
+        o.close()
+
+
+@pytest.mark.parametrize("per_launch", [1, 3])
+def test_arrival_split_into_launches_equals_one_launch(per_launch, monkeypatch):
+    """The arrival pass sent as consecutive launches over ranges of its
+    workgroups (as the library does for very large tables) writes the same
+    gradients, the same per-workgroup partials and hence the same sum of
+    squares, bit for bit, as one launch over the whole table; the update that
+    follows is then identical too."""
+    wl = _workload([W.BF16, W.F32, W.F16], seed_offset=41, n=40)
+    wl = replace(wl, tensors=[replace(t, numel=max(t.numel, 3000)) for t in wl.tensors])
+    # at most 8,192 elements per arrival workgroup: several launches of
+    # `per_launch` workgroups each
+    assert sum(t.numel for t in wl.tensors if t.trainable) > 8 * 8192
+    states, opts, incs = [], [], []
+    for cut in ("0", str(per_launch)):
+        monkeypatch.setenv("SOMAOPT_PASS3_SLICE_BLOCKS", cut)
+        st = allocate(wl)
+        fill_grads(wl, st, 1)
+        inc = _incoming(wl, st, False)
+        opt = make_handle(wl, st)
+        opt.register_arrival(inc)
+        states.append(st)
+        opts.append(opt)
+        incs.append(inc)
+    for k, acc in ((1, True), (2, False), (3, True)):
+        for inc in incs:
+            for i, t in enumerate(wl.tensors):
+                if t.trainable:
+                    inc[i].copy_(W.grad_values(wl, i, 70 + k, "cuda"))
+        for o in opts:
+            o.arrival_sqnorm(acc)
+            o.fused_adamw_step()
+        torch.cuda.synchronize()
+        s0, t0 = opts[0].read_stats()
+        s1, t1 = opts[1].read_stats()
+        assert s0.sumsq == s1.sumsq and t0 == t1 == [k]
+        for name in "pgmv":
+            for a, b in zip(getattr(states[0], name), getattr(states[1], name)):
+                assert np.array_equal(_bits(host(a)), _bits(host(b))), f"step {k}: {name} differs"
     for o in opts:
         o.close()
