@@ -254,7 +254,10 @@ int somaopt_fused_adamw_step(somaopt_handle* h, void* stream);
  * buffer may overlap any of those or any gradient (incoming buffers may
  * overlap each other).  Builds a device table (synchronizes `stream` once).
  * SOMAOPT_E_INVALID on a bad pointer, overlap or count; SOMAOPT_E_STATE if
- * already registered.
+ * already registered.  Tuning (optional environment, read here):
+ * SOMAOPT_PASS3_SLICE_BLOCKS = arrival-pass workgroups per launch above which
+ * the pass is split into several launches (65536; 0: always one launch); the
+ * statistics do not depend on the split.
  *
  * somaopt_arrival_sqnorm: for every trainable descriptor
  *     accumulate = 0:  grad <- incoming                      (bitwise copy)
