@@ -14,7 +14,9 @@ gradients.  Element comparisons cover every element:
   that tensor alone from its regenerated seeded inputs and the steps' global
   clip coefficients, streamed piece by piece; steps 3..10 follow sampled
   windows.  This covers the update pass's split into 13 launches and the cuts
-  between shards element by element.
+  between shards element by element;
+* one tensor of 2^32 + 3*2^20 + 5 elements: every element after step 1,
+  windows across 2^31 and 2^32 elements after step 2.
 
 Gradient buffers are checked unchanged on the device against a clone.
 """
@@ -495,3 +497,72 @@ def test_action_expert_arrival_full_size():
     log(f"[fullsize] arrival: tensor-wise rel err p={worst[0]:.2e} m={worst[1]:.2e} v={worst[2]:.2e}")
     opt.close()
     del p, g, m, v, inc
+
+
+def test_single_tensor_past_two_to_the_32_elements():
+    """One tensor of 2^32 + 3*2^20 + 5 elements (bf16 gradients, fp32 state:
+    60 GB on the device), stepped as the captured graph: its segments, the
+    update pass's launches and the byte offsets cross 2^31 and 2^32 elements,
+    and the last segment ends in a ragged scalar tail.  The global norm comes
+    from the oracle over every gradient on the host; after step 1 every element
+    of p, m and v is compared with the oracle run on host copies of the initial
+    weights and the gradients (streamed piece by piece), after step 2 (same
+    gradients) windows at the start, across both boundaries and at the end;
+    the gradients are compared bit for bit with their host copy at the end."""
+    from tensor_optimizer_step_amd import somaopt
+    n = (1 << 32) + 3 * (1 << 20) + 5
+    lr, wd, max_norm, divisor = 5e-6, 0.01, 1.0, 2.0
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4242)
+    p = torch.randn(n, generator=gen, device="cuda").mul_(0.02)
+    g = torch.randn(n, generator=gen, device="cuda", dtype=torch.bfloat16).mul_(0.05)
+    m = torch.zeros(n, device="cuda")
+    v = torch.zeros(n, device="cuda")
+    torch.cuda.synchronize()
+    log(f"[fullsize] single tensor: {n} elements allocated")
+    p0 = p.cpu().numpy()
+    g_host = W.to_numpy_grad(g)
+    pieces = [(a, min(a + PIECE, n)) for a in range(0, n, PIECE)]
+    total = host_sumsq([g_host[a:b] for a, b in pieces], divisor)
+    coef = O.clip_coefficient(float(np.sqrt(total)), max_norm)
+    assert coef < 1.0   # the step clips
+    log(f"[fullsize] single tensor: host norm {np.sqrt(total):.6f}, coefficient {coef:.6e}")
+    grp = O.Group(lr, wd, 0.9, 0.999, 1e-8)   # the same hyperparameters, for the oracle
+    hp = {"lr": lr, "weight_decay": wd, "beta1": 0.9, "beta2": 0.999, "eps": 1e-8}
+    opt = somaopt.FusedAdamW([p], [g], [m], [v], [0], [hp], max_norm, divisor)
+    assert opt.plan_info().pass2_launches > 1
+    opt.capture()
+    opt.replay()
+    torch.cuda.synchronize()
+    stats, steps = opt.read_stats()
+    assert steps == [1]
+    assert_norm(stats.norm, float(np.sqrt(total)))
+
+    def piece(ab):
+        a, b = ab
+        want = O.update_elements(p0[a:b], np.zeros(b - a), np.zeros(b - a), g_host[a:b], coef, divisor, grp, 1)
+        return [assert_close(f"single tensor step 1 {k}[{a}:{b}]", dt[a:b].cpu().numpy(), w)
+                for k, dt, w in zip("pmv", (p, m, v), want)]
+
+    worst = [0.0, 0.0, 0.0]
+    with ThreadPoolExecutor(WORKERS) as ex:
+        for r in ex.map(piece, pieces):
+            worst = [max(x, y) for x, y in zip(worst, r)]
+    log(f"[fullsize] single tensor: every element after step 1 within the bar; tensor-wise rel err "
+        f"p={worst[0]:.2e} m={worst[1]:.2e} v={worst[2]:.2e}")
+
+    opt.replay()
+    torch.cuda.synchronize()
+    stats, steps = opt.read_stats()
+    assert steps == [2]
+    assert_norm(stats.norm, float(np.sqrt(total)))
+    for a in (0, (1 << 31) - WINDOW // 2, (1 << 32) - WINDOW // 2, n - WINDOW):
+        b = a + WINDOW
+        st = (np.asarray(p0[a:b], np.float64), np.zeros(WINDOW), np.zeros(WINDOW))
+        for k in (1, 2):
+            st = O.update_elements(*st, g_host[a:b], coef, divisor, grp, k)
+        for name, dt, w in zip("pmv", (p, m, v), st):
+            assert_close(f"single tensor step 2 {name}[{a}:{b}]", dt[a:b].cpu().numpy(), w)
+    assert np.array_equal(W.to_numpy_grad(g), g_host), "gradient buffer was written"
+    log("[fullsize] single tensor: step-2 windows across 2^31 and 2^32 within the bar; gradients unchanged")
+    opt.close()
