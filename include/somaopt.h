@@ -168,8 +168,8 @@ typedef struct somaopt_handle somaopt_handle;
  * a buffer that is not device memory of the current device or that runs past
  * the end of its allocation (skipped if SOMAOPT_SKIP_POINTER_CHECK=1).
  * Tuning (optional environment): SOMAOPT_PASS1_CHUNK, SOMAOPT_PASS2_CHUNK =
- * maximum elements per workgroup of the norm / update pass (the update pass
- * at most 2^26); SOMAOPT_PASS1_WG_PER_CU, SOMAOPT_PASS2_WG_PER_CU = resident
+ * maximum elements per workgroup of the norm / update pass (each at most
+ * 2^26; larger values are lowered to it); SOMAOPT_PASS1_WG_PER_CU, SOMAOPT_PASS2_WG_PER_CU = resident
  * workgroups per compute unit (0: no limit; unset: chosen from the table
  * shape, reported in somaopt_plan_info); SOMAOPT_SEGMENT_COST,
  * SOMAOPT_UPDATE_SEGMENT_COST = elements charged per segment when short
@@ -374,7 +374,7 @@ int somaopt_get_plan_info(const somaopt_handle* h, somaopt_plan_info* out);
  * build the plan of one pass (pass = 1: norm pass, 2: update pass) without
  * touching a GPU.  Writes up to `cap` rows to `segs` (may be NULL) and the
  * counts to `info` (may be NULL).  pass1_chunk / pass2_chunk <= 0 select the
- * defaults.  Returns the number of segments of that pass, or a negative status.
+ * defaults; values above 2^26 are lowered to 2^26, as at init.  Returns the number of segments of that pass, or a negative status.
  */
 int64_t somaopt_debug_plan(const somaopt_tensor_desc* descs, int64_t n_tensors, int32_t n_groups,
                            int32_t pass, int64_t pass1_chunk, int64_t pass2_chunk,

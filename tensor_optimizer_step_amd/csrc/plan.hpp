@@ -113,20 +113,20 @@ int validate_arrival(const somaopt_tensor_desc* d, int64_t n, const void* const*
 Plan build_plan(const somaopt_tensor_desc* d, int64_t n, int pass, int64_t chunk,
                 int64_t segment_cost = -1, const void* const* incoming = nullptr);
 
-// Largest update-pass segment: its vector body is addressed with 32-bit byte
-// offsets (16 bytes per 4-element vector) by the buffer instructions.
-constexpr int64_t kMaxPass2Chunk = int64_t(1) << 26;
+// Largest segment of any pass: every kernel addresses a segment's vector body
+// through a buffer resource whose size and lane offsets are 32-bit byte counts
+// (at 2^30 fp32 elements a segment's 2^32 bytes would wrap to 0); 2^26
+// elements keep every segment below 2^28 bytes.
+constexpr int64_t kMaxChunk = int64_t(1) << 26;
 
 // Normalise a requested chunk: positive multiple of 8, at least 256 elements,
 // at most `max_chunk`.
-int64_t normalise_chunk(int64_t requested, int64_t dflt, int64_t max_chunk = int64_t(1) << 30);
+int64_t normalise_chunk(int64_t requested, int64_t dflt, int64_t max_chunk = kMaxChunk);
 
-// Segment length of the arrival pass: the norm pass's chunk, capped like the
-// update pass's because the arrival kernel also addresses each segment's
-// vector body through buffer resources with 32-bit byte offsets (16 bytes per
-// vector; at 2^30 fp32 elements a segment's 2^32 bytes would wrap to 0).
+// Segment length of the arrival pass: the norm pass's chunk (kept within
+// kMaxChunk here too, for a chunk given from elsewhere).
 inline int64_t arrival_chunk(int64_t pass1_chunk) {
-    return pass1_chunk < kMaxPass2Chunk ? pass1_chunk : kMaxPass2Chunk;
+    return pass1_chunk < kMaxChunk ? pass1_chunk : kMaxChunk;
 }
 
 // True when at least half of the plan's elements lie in segments of the full

@@ -81,7 +81,7 @@ static void check_arrival_offsets(const std::vector<somaopt_tensor_desc>& d, std
         ia = (ia + gsz * (uintptr_t)t.numel + 512) & ~uintptr_t(255);
     }
     const int64_t chunk = arrival_chunk(normalise_chunk(int64_t(1) << 40, kDefaultPass1Chunk));
-    EXPECT(chunk <= kMaxPass2Chunk, "arrival chunk %lld above the buffer-offset limit", (long long)chunk);
+    EXPECT(chunk <= kMaxChunk, "arrival chunk %lld above the buffer-offset limit", (long long)chunk);
     Plan p = build_plan(big.data(), (int64_t)big.size(), 3, chunk, kSegmentCost, inc.data());
     for (const PlanSeg& g : p.segs) {
         EXPECT(g.numel <= chunk, "arrival segment of %lld elements", (long long)g.numel);

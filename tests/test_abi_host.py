@@ -174,6 +174,26 @@ def test_plan_many_small_tensors_pack_into_few_blocks():
     assert info.pass2_blocks == len(sizes)
 
 
+def test_chunks_stay_within_32_bit_buffer_offsets():
+    """Every pass addresses a segment's vector body through a buffer resource
+    with 32-bit byte sizes and offsets: a requested chunk of 2^30 elements is
+    lowered to 2^26 for the norm pass as for the update pass, so no segment's
+    body reaches 2^31 bytes (at 2^30 fp32 elements it would be 2^32 bytes,
+    which wraps to 0 and would silently read zeros)."""
+    n = (1 << 29) + 12345
+    rows = _rows([n, 1000], dtypes=[S.F32, S.BF16])
+    for pass_ in (1, 2):
+        segs, info = S.debug_plan(rows, 1, pass_, 1 << 30, 1 << 30)
+        assert info.pass1_chunk == 1 << 26 and info.pass2_chunk == 1 << 26
+        assert max(sg.numel for sg in segs) <= 1 << 26
+        assert max(16 * sg.nvec for sg in segs) < 1 << 31
+        # the segments still tile every element of every tensor
+        covered = {}
+        for sg in segs:
+            covered[sg.tensor] = covered.get(sg.tensor, 0) + sg.numel
+        assert covered == {0: n, 1: 1000}
+
+
 def test_occupancy_follows_the_table_shape():
     """Large tensors (full-length segments) get the streaming occupancy limits
     (6 norm-pass and 2 update-pass workgroups per CU); a table of many small
