@@ -257,7 +257,10 @@ int somaopt_fused_adamw_step(somaopt_handle* h, void* stream);
  * already registered.  Tuning (optional environment, read here):
  * SOMAOPT_PASS3_SLICE_BLOCKS = arrival-pass workgroups per launch above which
  * the pass is split into several launches (65536; 0: always one launch); the
- * statistics do not depend on the split.
+ * statistics do not depend on the split.  SOMAOPT_PASS3_WG_PER_CU = resident
+ * arrival-pass workgroups per compute unit, both modes (0: no limit; unset:
+ * for a streaming table six when copying and four when accumulating, none
+ * for a packed one).
  *
  * somaopt_arrival_sqnorm: for every trainable descriptor
  *     accumulate = 0:  grad <- incoming                      (bitwise copy)

@@ -26,6 +26,13 @@ constexpr int kVecsPerThread = 4;
 //    each starting with dependent descriptor loads): the update pass needs
 //    four per CU to hide those latencies, and the norm pass no limit.
 constexpr int kPass1WgPerCuStreaming = 6;
+// The arrival pass over a streaming table: as the norm pass when it copies the
+// arriving values (one read, one write per element), four per CU when it
+// accumulates (two reads, one write).  Measured on MI355X, 6.7e9 bf16
+// gradients accumulated: 6.80 ms at six, 6.44 at three or four, 8.00 at two;
+// copied: 4.16 ms at six, 5.30 at three or four.  On the 302M-element table
+// the accumulate step is the same at four and six (1.525 ms).
+constexpr int kPass3WgPerCuAccumulate = 4;
 constexpr int kPass2WgPerCuStreaming = 2;
 constexpr int kPass2WgPerCuPacked = 4;
 // Workgroups per update-pass launch.  A larger pass is split into consecutive

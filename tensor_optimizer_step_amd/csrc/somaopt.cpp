@@ -46,7 +46,8 @@ struct somaopt_handle {
     Seg3* d_seg3 = nullptr;
     uint32_t* d_blk3 = nullptr;
     uint32_t nblk3 = 0;
-    uint32_t lds3 = 0;
+    uint32_t lds3 = 0;             // LDS reserved per arrival-pass workgroup, copying
+    uint32_t lds3_acc = 0;         // and accumulating
     uint32_t per3 = 0;             // arrival-pass workgroups per launch (0: one launch)
     double* d_partials3 = nullptr;
     double* d_partials3b = nullptr;
@@ -580,7 +581,12 @@ int somaopt_register_arrival(somaopt_handle* h, const void* const* incoming, int
     if (hipDeviceGetAttribute(&lds_per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, h->device) !=
         hipSuccess)
         lds_per_cu = 0;
-    h->lds3 = occupancy_lds(lds_per_cu, streaming_plan(p3) ? kPass1WgPerCuStreaming : 0);
+    const int64_t w3 = env_int("SOMAOPT_PASS3_WG_PER_CU", -1);
+    const bool stream3 = streaming_plan(p3);
+    h->lds3 = occupancy_lds(lds_per_cu, w3 >= 0 ? (int)std::min<int64_t>(w3, 64)
+                                                : (stream3 ? kPass1WgPerCuStreaming : 0));
+    h->lds3_acc = occupancy_lds(lds_per_cu, w3 >= 0 ? (int)std::min<int64_t>(w3, 64)
+                                                    : (stream3 ? kPass3WgPerCuAccumulate : 0));
     const int64_t slice = env_int("SOMAOPT_PASS3_SLICE_BLOCKS", -1);
     h->per3 = slice >= 0 ? (uint32_t)std::min<int64_t>(slice, 0xFFFFFFFFll) : kPass3SliceBlocks;
     return SOMAOPT_OK;
@@ -680,7 +686,7 @@ int launch_arrival_pass(somaopt_handle* h, int advance, int32_t accumulate, hipS
     a.n_groups = h->n_groups;
     a.advance = advance;
     a.accumulate = accumulate;
-    a.lds_bytes = h->lds3;
+    a.lds_bytes = accumulate ? h->lds3_acc : h->lds3;
     hipError_t e = launch_pass3(a, h->per3, s);
     return e == hipSuccess ? SOMAOPT_OK : hip_fail(e, "arrival pass launch");
 }
