@@ -18,10 +18,14 @@ constexpr int kVecsPerThread = 4;
 // data; a launch reserves a share of the CU's LDS so that no more than this
 // many workgroups are resident at once.  Measured on MI355X:
 //  - tables of large tensors (a workgroup streams one full segment): the
-//    4-read / 3-write update stream sustains its highest HBM bandwidth with two
-//    256-thread workgroups (8 waves) per CU, about 10% above the unrestricted
-//    occupancy of five, because fewer concurrent streams keep DRAM rows open
-//    longer; the read-only norm pass prefers six (7% faster on 7B-scale state);
+//    4-read / 3-write update stream sustains its highest HBM bandwidth with
+//    about 114 KB of loads in flight per CU: two 256-thread workgroups per CU
+//    over 4096-element segments were about 10% above the
+//    unrestricted occupancy of five, because fewer concurrent streams keep
+//    DRAM rows open longer; four per CU over the half-length segments of
+//    kStreamingPass2Chunk (the same bytes in flight) are another 1.5% faster
+//    at 7B scale (three or more per CU over 4096 elements: 8-9% slower); the
+//    read-only norm pass prefers six (7% faster on 7B-scale state);
 //  - tables of many small tensors (a workgroup walks several short segments,
 //    each starting with dependent descriptor loads): the update pass needs
 //    four per CU to hide those latencies, and the norm pass no limit.
@@ -33,7 +37,7 @@ constexpr int kPass1WgPerCuStreaming = 6;
 // copied: 4.16 ms at six, 5.30 at three or four.  On the 302M-element table
 // the accumulate step is the same at four and six (1.525 ms).
 constexpr int kPass3WgPerCuAccumulate = 4;
-constexpr int kPass2WgPerCuStreaming = 2;
+constexpr int kPass2WgPerCuStreaming = 4;
 constexpr int kPass2WgPerCuPacked = 4;
 // Workgroups per update-pass launch.  A larger pass is split into consecutive
 // launches of about this many workgroups each, on the same stream.  The
@@ -42,11 +46,13 @@ constexpr int kPass2WgPerCuPacked = 4;
 // so the single front of addresses that all CUs stream through splits into
 // eight, and DRAM rows whose data is spread over several XCDs' workgroups are
 // opened more than once.  A launch boundary brings the XCDs back together.
-// Measured on MI355X over 6.7e9 elements (1.65M workgroups, 28.9 ms in one
-// launch): 27.72 ms at 131072 per launch, 27.70 at 65536, 27.97 at 16384 (each
-// boundary costs about 4 us of ramp-down and ramp-up); a 302M-element table
-// (73,780 workgroups) is unchanged by splitting, so it stays one launch.
-constexpr uint32_t kPass2SliceBlocks = 131072;
+// Measured on MI355X over 6.7e9 elements in 4096-element workgroups (1.65M,
+// 28.9 ms in one launch): 27.72 ms at 131072 per launch, 27.70 at 65536, 27.97
+// at 16384 (each boundary costs about 4 us of ramp-down and ramp-up); in
+// 2048-element workgroups 262144 and 131072 per launch give the same time
+// (27.457 and 27.461 ms), so a launch keeps covering about 5.4e8 elements; a
+// 302M-element table (147,559 workgroups) stays one launch.
+constexpr uint32_t kPass2SliceBlocks = 262144;
 // Workgroups per arrival-pass launch (8,192 elements each), for the same
 // reason: the arrival pass reads and writes like the update pass.  Measured
 // on MI355X, 6.7e9 bf16 gradients accumulated (822K workgroups): 7.01 ms in

@@ -266,4 +266,11 @@ bool streaming_plan(const Plan& p) {
     return total > 0 && 2 * full >= total;
 }
 
+Plan build_update_plan(const somaopt_tensor_desc* d, int64_t n, int64_t requested, int64_t segment_cost) {
+    if (requested > 0) return build_plan(d, n, 2, normalise_chunk(requested, kDefaultPass2Chunk), segment_cost);
+    Plan p = build_plan(d, n, 2, kDefaultPass2Chunk, segment_cost);
+    if (streaming_plan(p)) p = build_plan(d, n, 2, kStreamingPass2Chunk, segment_cost);
+    return p;
+}
+
 }  // namespace somaopt

@@ -61,6 +61,18 @@ static_assert(sizeof(Seg2) == 64, "Seg2 layout");
 // longer or persistent workgroups by 10-20% in sustained HBM bandwidth.
 constexpr int64_t kDefaultPass1Chunk = 8192;
 constexpr int64_t kDefaultPass2Chunk = 4096;
+// Update-pass segments of a streaming table (most elements in full-length
+// segments): half a batch, so that each thread's four vectors are two real
+// ones and two that the buffer bounds turn into no memory access, at four
+// resident workgroups per CU instead of two: the same bytes in flight per CU
+// in twice as many shorter workgroups.  Measured on MI355X in one process
+// against 4096 at two per CU, four times on two boxes: the 7B update pass
+// 27.28-27.46 against 27.74-27.89 ms (1.5-1.7%), the 302M-element one 0.3-1.5%
+// faster; 3072 at three per CU and kernels built for exactly two vectors per
+// thread or 128-thread workgroups were 4-13% slower.  Tables of small
+// tensors keep 4096 (at 2048 the 20,000-tensor update pass took 134.5 against
+// 128.0 us).
+constexpr int64_t kStreamingPass2Chunk = 2048;
 // Packing cost of one segment, in elements: a segment costs about one memory
 // latency before its loads are in flight.  Measured on MI355X: for the norm
 // (and arrival) pass 1024 beats 64 by 3% per step on the 20,000-tensor
@@ -132,6 +144,11 @@ inline int64_t arrival_chunk(int64_t pass1_chunk) {
 // True when at least half of the plan's elements lie in segments of the full
 // chunk length, i.e. most workgroups stream one long run of one tensor.
 bool streaming_plan(const Plan& p);
+
+// The update pass's plan.  `requested` > 0: segments of that many elements
+// (normalised).  Otherwise segments of kDefaultPass2Chunk, re-planned with
+// kStreamingPass2Chunk when that plan streams.
+Plan build_update_plan(const somaopt_tensor_desc* d, int64_t n, int64_t requested, int64_t segment_cost);
 
 inline int64_t grad_elem_bytes(int32_t dtype) { return dtype == SOMAOPT_F32 ? 4 : 2; }
 

@@ -314,9 +314,8 @@ int64_t somaopt_debug_plan(const somaopt_tensor_desc* descs, int64_t n_tensors, 
     int rc = validate_host(descs, n_tensors, n_groups, err, &c);
     if (rc != SOMAOPT_OK) return fail(rc, err);
     const int64_t ch1 = normalise_chunk(pass1_chunk, kDefaultPass1Chunk);
-    const int64_t ch2 = normalise_chunk(pass2_chunk, kDefaultPass2Chunk);
     Plan p1 = build_plan(descs, n_tensors, 1, ch1);
-    Plan p2 = build_plan(descs, n_tensors, 2, ch2);
+    Plan p2 = build_update_plan(descs, n_tensors, pass2_chunk, kUpdateSegmentCost);
     if (info) fill_info(info, n_tensors, c, p1, p2);
     const Plan& p = pass == 1 ? p1 : p2;
     if (segs) {
@@ -362,11 +361,10 @@ int somaopt::init_table(const somaopt_tensor_desc* descs, int64_t n_tensors, con
     rc = validate_host(descs, n_tensors, n_groups, err, &counts);
     if (rc) return fail(rc, err);
     const int64_t ch1 = normalise_chunk(env_int("SOMAOPT_PASS1_CHUNK", 0), kDefaultPass1Chunk);
-    const int64_t ch2 = normalise_chunk(env_int("SOMAOPT_PASS2_CHUNK", 0), kDefaultPass2Chunk);
     const int64_t cost1 = std::max<int64_t>(0, env_int("SOMAOPT_SEGMENT_COST", kSegmentCost));
     const int64_t cost2 = std::max<int64_t>(0, env_int("SOMAOPT_UPDATE_SEGMENT_COST", kUpdateSegmentCost));
     Plan p1 = build_plan(descs, n_tensors, 1, ch1, cost1);
-    Plan p2 = build_plan(descs, n_tensors, 2, ch2, cost2);
+    Plan p2 = build_update_plan(descs, n_tensors, env_int("SOMAOPT_PASS2_CHUNK", 0), cost2);
     if (p1.segs.size() >= 0xFFFFFFFFull || p2.segs.size() >= 0xFFFFFFFFull)
         return fail(SOMAOPT_E_INVALID, "too many segments for 32-bit indices");
     // A dispatch holds fewer than 2^32 work-items.

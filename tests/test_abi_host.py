@@ -125,7 +125,7 @@ def test_plan_covers_every_element_once(pass_):
 
 def test_plan_aligned_tensors_use_vectors():
     rows = _rows([1000, 4096, 13], [S.F32, S.BF16, S.F32])
-    segs, info = S.debug_plan(rows, 1, 2, 0, 0)
+    segs, info = S.debug_plan(rows, 1, 2, 0, 4096)
     assert info.scalar_segments == 0
     assert all(s.vec_elems == 4 for s in segs)
     assert segs[0].head == 0 and segs[0].nvec == 250 and segs[0].tail == 0
@@ -195,31 +195,36 @@ def test_chunks_stay_within_32_bit_buffer_offsets():
 
 
 def test_occupancy_follows_the_table_shape():
-    """Large tensors (full-length segments) get the streaming occupancy limits
-    (6 norm-pass and 2 update-pass workgroups per CU); a table of many small
-    tensors, whose workgroups walk several short segments, gets 4 update-pass
-    workgroups per CU and no norm-pass limit."""
+    """Large tensors (full-length segments) get the streaming plan: 6 norm-pass
+    workgroups per CU, and update-pass segments of 2048 elements at 4 per CU;
+    a table of many small tensors, whose workgroups walk several short
+    segments, keeps 4096-element update segments at 4 per CU and no norm-pass
+    limit.  An explicit update chunk is used as given."""
     big = _rows([1 << 20] * 4 + [1024] * 3, dtypes=[S.BF16] * 7)
-    _, info = S.debug_plan(big, 1, 2)
-    assert (info.pass1_wg_per_cu, info.pass2_wg_per_cu) == (6, 2)
+    segs, info = S.debug_plan(big, 1, 2)
+    assert (info.pass1_wg_per_cu, info.pass2_wg_per_cu, info.pass2_chunk) == (6, 4, 2048)
+    assert max(sg.numel for sg in segs) == 2048 and info.pass2_blocks == 4 * 512 + 3
     rng = np.random.default_rng(3)
     small = _rows([int(x) for x in rng.integers(1, 4097, size=2000)])
     _, info = S.debug_plan(small, 1, 2)
-    assert (info.pass1_wg_per_cu, info.pass2_wg_per_cu) == (0, 4)
+    assert (info.pass1_wg_per_cu, info.pass2_wg_per_cu, info.pass2_chunk) == (0, 4, 4096)
     # half of the elements in full segments is still a streaming table
     mixed = _rows([8192 * 8] + [100] * 600)
     _, info = S.debug_plan(mixed, 1, 2)
-    assert info.pass2_wg_per_cu == 2
+    assert (info.pass2_wg_per_cu, info.pass2_chunk) == (4, 2048)
+    # an explicit chunk is not re-planned
+    _, info = S.debug_plan(big, 1, 2, 0, 4096)
+    assert (info.pass2_chunk, info.pass2_blocks) == (4096, 4 * 256 + 3)
 
 
 def test_update_pass_launch_split():
-    """An update pass above 131072 workgroups is split into launches of equal
+    """An update pass above 262144 workgroups is split into launches of equal
     size; at or below it stays one launch; an empty pass has none."""
-    _, info = S.debug_plan(_rows([131072 * 4096], dtypes=[S.BF16]), 1, 2)
-    assert (info.pass2_blocks, info.pass2_launches) == (131072, 1)
-    _, info = S.debug_plan(_rows([131072 * 4096 + 1], dtypes=[S.BF16]), 1, 2)
-    assert (info.pass2_blocks, info.pass2_launches) == (131073, 2)
-    _, info = S.debug_plan(_rows([100 * 4096] * 5), 1, 2)
+    _, info = S.debug_plan(_rows([262144 * 2048], dtypes=[S.BF16]), 1, 2)
+    assert (info.pass2_blocks, info.pass2_launches) == (262144, 1)
+    _, info = S.debug_plan(_rows([262144 * 2048 + 1], dtypes=[S.BF16]), 1, 2)
+    assert (info.pass2_blocks, info.pass2_launches) == (262145, 2)
+    _, info = S.debug_plan(_rows([100 * 2048] * 5), 1, 2)
     assert (info.pass2_blocks, info.pass2_launches) == (500, 1)
     _, info = S.debug_plan([], 1, 2)
     assert info.pass2_launches == 0
