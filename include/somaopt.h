@@ -193,8 +193,8 @@ int somaopt_init_tensor_table(const somaopt_tensor_desc* descs, int64_t n_tensor
  * device allocation (it uploads the tables with hipMemcpyAsync on `stream`
  * and waits for that stream, like the allocating call).
  *   - Limit: the array holds 32 MiB (33,554,432 bytes) per device, held from
- *     the first use until the process ends.  That fits tables of about 1.5e9
- *     elements in large tensors (the 302M-element action head needs 3.9 MB);
+ *     the first use until the process ends.  That fits tables of about 8.9e8
+ *     elements in large tensors (the 302M-element action head needs 11.4 MB);
  *     a table that needs more is refused with SOMAOPT_E_INVALID and a message
  *     giving both sizes, before anything touches the device.
  *   - Sharing: every no-allocation handle of a device uses the same array.
