@@ -255,11 +255,13 @@ int somaopt_fused_adamw_step(somaopt_handle* h, void* stream);
  * overlap each other).  Builds a device table (synchronizes `stream` once).
  * SOMAOPT_E_INVALID on a bad pointer, overlap or count; SOMAOPT_E_STATE if
  * already registered.  Tuning (optional environment, read here):
+ * SOMAOPT_PASS3_CHUNK = maximum elements per arrival-pass workgroup (unset:
+ * the norm pass's, halved to 4096 for a table of large tensors, at most 2^26);
  * SOMAOPT_PASS3_SLICE_BLOCKS = arrival-pass workgroups per launch above which
- * the pass is split into several launches (65536; 0: always one launch); the
+ * the pass is split into several launches (131072; 0: always one launch); the
  * statistics do not depend on the split.  SOMAOPT_PASS3_WG_PER_CU = resident
  * arrival-pass workgroups per compute unit, both modes (0: no limit; unset:
- * for a streaming table six when copying and four when accumulating, none
+ * for a streaming table none when copying and six when accumulating, none
  * for a packed one).
  *
  * somaopt_arrival_sqnorm: for every trainable descriptor

@@ -30,13 +30,16 @@ constexpr int kVecsPerThread = 4;
 //    each starting with dependent descriptor loads): the update pass needs
 //    four per CU to hide those latencies, and the norm pass no limit.
 constexpr int kPass1WgPerCuStreaming = 6;
-// The arrival pass over a streaming table: as the norm pass when it copies the
-// arriving values (one read, one write per element), four per CU when it
-// accumulates (two reads, one write).  Measured on MI355X, 6.7e9 bf16
-// gradients accumulated: 6.80 ms at six, 6.44 at three or four, 8.00 at two;
-// copied: 4.16 ms at six, 5.30 at three or four.  On the 302M-element table
-// the accumulate step is the same at four and six (1.525 ms).
-constexpr int kPass3WgPerCuAccumulate = 4;
+// The arrival pass over a streaming table (4096-element segments,
+// kStreamingPass3Chunk): no limit when it copies the arriving values (one
+// read, one write per element), six per CU when it accumulates (two reads,
+// one write).  Measured on MI355X, 6.7e9 bf16 gradients: accumulated 6.25 ms
+// at six, 6.71 at eight, 6.83 unlimited, 7.38 at four; copied 4.04 ms
+// unlimited, 4.13 at eight, 4.32 at six.  302M elements: accumulated 0.272 ms
+// at six, 0.284 unlimited; copied 0.176 ms unlimited, 0.194 at six.  (Over
+// the previous 8192-element segments: four and six per CU respectively.)
+constexpr int kPass3WgPerCuAccumulate = 6;
+constexpr int kPass3WgPerCuCopy = 0;
 constexpr int kPass2WgPerCuStreaming = 4;
 constexpr int kPass2WgPerCuPacked = 4;
 // Workgroups per update-pass launch.  A larger pass is split into consecutive
@@ -53,12 +56,13 @@ constexpr int kPass2WgPerCuPacked = 4;
 // (27.457 and 27.461 ms), so a launch keeps covering about 5.4e8 elements; a
 // 302M-element table (147,559 workgroups) stays one launch.
 constexpr uint32_t kPass2SliceBlocks = 262144;
-// Workgroups per arrival-pass launch (8,192 elements each), for the same
-// reason: the arrival pass reads and writes like the update pass.  Measured
-// on MI355X, 6.7e9 bf16 gradients accumulated (822K workgroups): 7.01 ms in
-// one launch, 6.86 at 131072 per launch, 6.81 at 65536, 6.78 at 32768; the
-// 302M-element table (36,890 workgroups) stays one launch.
-constexpr uint32_t kPass3SliceBlocks = 65536;
+// Workgroups per arrival-pass launch, for the same reason: the arrival pass
+// reads and writes like the update pass.  Measured on MI355X, 6.7e9 bf16
+// gradients accumulated in 8,192-element workgroups (822K): 7.01 ms in one
+// launch, 6.86 at 131072 per launch, 6.81 at 65536, 6.78 at 32768.  With
+// 4,096-element workgroups a launch of 131072 keeps covering about 5.4e8
+// elements; the 302M-element table (73,780 workgroups) stays one launch.
+constexpr uint32_t kPass3SliceBlocks = 131072;
 // Number of launches for `n_blocks` workgroups at `per_launch` per launch
 // (0: one launch); every launch gets the same count, the last possibly fewer.
 inline int64_t update_launches(int64_t n_blocks, int64_t per_launch) {

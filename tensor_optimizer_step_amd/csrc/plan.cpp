@@ -266,6 +266,17 @@ bool streaming_plan(const Plan& p) {
     return total > 0 && 2 * full >= total;
 }
 
+Plan build_arrival_plan(const somaopt_tensor_desc* d, int64_t n, int64_t pass1_chunk, int64_t requested,
+                        const void* const* incoming) {
+    if (requested > 0)
+        return build_plan(d, n, 3, normalise_chunk(requested, kDefaultPass1Chunk), kSegmentCost, incoming);
+    const int64_t chunk = arrival_chunk(pass1_chunk);
+    Plan p = build_plan(d, n, 3, chunk, kSegmentCost, incoming);
+    if (streaming_plan(p) && chunk > kStreamingPass3Chunk)
+        p = build_plan(d, n, 3, kStreamingPass3Chunk, kSegmentCost, incoming);
+    return p;
+}
+
 Plan build_update_plan(const somaopt_tensor_desc* d, int64_t n, int64_t requested, int64_t segment_cost) {
     if (requested > 0) return build_plan(d, n, 2, normalise_chunk(requested, kDefaultPass2Chunk), segment_cost);
     Plan p = build_plan(d, n, 2, kDefaultPass2Chunk, segment_cost);

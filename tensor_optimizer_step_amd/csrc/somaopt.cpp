@@ -539,7 +539,7 @@ int somaopt_register_arrival(somaopt_handle* h, const void* const* incoming, int
             if (rc) return rc;
         }
     }
-    Plan p3 = build_plan(d, n_tensors, 3, arrival_chunk(h->pass1_chunk), kSegmentCost, incoming);
+    Plan p3 = build_arrival_plan(d, n_tensors, h->pass1_chunk, env_int("SOMAOPT_PASS3_CHUNK", 0), incoming);
     if (p3.segs.size() >= 0xFFFFFFFFull || (uint64_t)p3.n_blocks() * kPass1Threads >= 0xFFFFFFFFull)
         return fail(SOMAOPT_E_INVALID, "arrival table too large for one dispatch");
     if (p3.block_first.size() < 2) p3.block_first = {0u, 0u};   // statistics even when nothing is trainable
@@ -582,7 +582,7 @@ int somaopt_register_arrival(somaopt_handle* h, const void* const* incoming, int
     const int64_t w3 = env_int("SOMAOPT_PASS3_WG_PER_CU", -1);
     const bool stream3 = streaming_plan(p3);
     h->lds3 = occupancy_lds(lds_per_cu, w3 >= 0 ? (int)std::min<int64_t>(w3, 64)
-                                                : (stream3 ? kPass1WgPerCuStreaming : 0));
+                                                : (stream3 ? kPass3WgPerCuCopy : 0));
     h->lds3_acc = occupancy_lds(lds_per_cu, w3 >= 0 ? (int)std::min<int64_t>(w3, 64)
                                                     : (stream3 ? kPass3WgPerCuAccumulate : 0));
     const int64_t slice = env_int("SOMAOPT_PASS3_SLICE_BLOCKS", -1);
