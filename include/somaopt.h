@@ -168,14 +168,16 @@ typedef struct somaopt_handle somaopt_handle;
  * a buffer that is not device memory of the current device or that runs past
  * the end of its allocation (skipped if SOMAOPT_SKIP_POINTER_CHECK=1).
  * Tuning (optional environment): SOMAOPT_PASS1_CHUNK, SOMAOPT_PASS2_CHUNK =
- * maximum elements per workgroup of the norm / update pass (each at most
- * 2^26; larger values are lowered to it); SOMAOPT_PASS1_WG_PER_CU, SOMAOPT_PASS2_WG_PER_CU = resident
+ * maximum elements per workgroup of the norm / update pass (unset: 8192, and
+ * for the update pass 4096, or 2048 when most elements lie in full-length
+ * segments; each at most 2^26, larger values are lowered to it);
+ * SOMAOPT_PASS1_WG_PER_CU, SOMAOPT_PASS2_WG_PER_CU = resident
  * workgroups per compute unit (0: no limit; unset: chosen from the table
  * shape, reported in somaopt_plan_info); SOMAOPT_SEGMENT_COST,
  * SOMAOPT_UPDATE_SEGMENT_COST = elements charged per segment when short
  * segments are packed into the norm / update pass's workgroups (1024, 4096);
  * SOMAOPT_PASS2_SLICE_BLOCKS = update-pass workgroups per launch above which
- * the pass is split into several launches (131072; 0: always one launch).
+ * the pass is split into several launches (262144; 0: always one launch).
  */
 int somaopt_init_tensor_table(const somaopt_tensor_desc* descs, int64_t n_tensors,
                               const somaopt_group* groups, int32_t n_groups,
@@ -228,7 +230,7 @@ int somaopt_grad_sqnorm(somaopt_handle* h, void* stream);
 
 /*
  * Update pass: one launch over every trainable segment (a pass of more than
- * 131072 workgroups, about 5.4e8 elements, goes out as consecutive launches
+ * 262144 workgroups, about 5.4e8 elements, goes out as consecutive launches
  * over ranges of its workgroups, each still spanning many tensors: see
  * somaopt_plan_info.pass2_launches); reads g, p, m, v and writes p, m, v using
  * the statistics the preceding somaopt_grad_sqnorm left on the device.  Landing page, paragraph 8: the last pass works from the
