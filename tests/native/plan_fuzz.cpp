@@ -22,20 +22,25 @@ static int fails = 0;
         }                                                 \
     } while (0)
 
-static void check_plan(const std::vector<somaopt_tensor_desc>& d, int pass, int64_t chunk) {
-    Plan p = build_plan(d.data(), (int64_t)d.size(), pass, chunk);
+// Every segment of a built plan lies inside one included tensor, at most
+// p.chunk long, in order, and the segments cover each included tensor once.
+// Pass 3 (arrival) includes every trainable tensor like pass 2; its vector
+// alignment is checked by check_arrival_offsets.
+static void check_built(const Plan& p, const std::vector<somaopt_tensor_desc>& d, int pass) {
+    const int64_t chunk = p.chunk;
     std::vector<int64_t> covered(d.size(), 0);
     std::vector<int64_t> next_off(d.size(), 0);
     for (size_t s = 0; s < p.segs.size(); ++s) {
         const PlanSeg& g = p.segs[s];
         const somaopt_tensor_desc& t = d[g.tensor];
-        EXPECT(t.trainable && (pass == 2 || t.owner), "segment of an excluded tensor %lld", (long long)g.tensor);
+        EXPECT(t.trainable && (pass != 1 || t.owner), "segment of an excluded tensor %lld", (long long)g.tensor);
         EXPECT(g.numel <= chunk && g.numel > 0, "segment size %lld", (long long)g.numel);
         EXPECT(g.numel == g.head + g.nvec * g.vec + g.tail, "segment arithmetic");
         EXPECT(g.offset == next_off[g.tensor], "segments out of order or overlapping");
         next_off[g.tensor] = g.offset + g.numel;
         covered[g.tensor] += g.numel;
-        if (g.vec && g.nvec > 0) {
+        EXPECT(16 * g.nvec < (int64_t(1) << 31), "segment body of %lld bytes", (long long)(16 * g.nvec));
+        if (pass != 3 && g.vec && g.nvec > 0) {
             const int64_t gsz = grad_elem_bytes(t.grad_dtype);
             const int64_t start = g.offset + g.head;
             if (pass == 1) {
@@ -56,10 +61,30 @@ static void check_plan(const std::vector<somaopt_tensor_desc>& d, int pass, int6
         EXPECT(p.block_first[g.block] <= s && s < p.block_first[g.block + 1], "block table");
     }
     for (size_t i = 0; i < d.size(); ++i) {
-        const bool want = d[i].trainable && d[i].numel > 0 && (pass == 2 || d[i].owner);
+        const bool want = d[i].trainable && d[i].numel > 0 && (pass != 1 || d[i].owner);
         EXPECT(covered[i] == (want ? d[i].numel : 0), "tensor %zu covered %lld of %lld", i,
                (long long)covered[i], (long long)d[i].numel);
     }
+}
+
+static void check_plan(const std::vector<somaopt_tensor_desc>& d, int pass, int64_t chunk) {
+    const Plan p = build_plan(d.data(), (int64_t)d.size(), pass, chunk);
+    EXPECT(p.chunk == chunk, "plan chunk %lld, asked %lld", (long long)p.chunk, (long long)chunk);
+    check_built(p, d, pass);
+}
+
+// The update plan the library builds by default: 4096-element segments, or
+// 2048 when that plan streams; an explicit chunk is kept.
+static void check_update_plan(const std::vector<somaopt_tensor_desc>& d) {
+    const int64_t n = (int64_t)d.size();
+    const bool streams = streaming_plan(build_plan(d.data(), n, 2, kDefaultPass2Chunk, kUpdateSegmentCost));
+    const Plan p = build_update_plan(d.data(), n, 0, kUpdateSegmentCost);
+    EXPECT(p.chunk == (streams ? kStreamingPass2Chunk : kDefaultPass2Chunk), "update plan chunk %lld",
+           (long long)p.chunk);
+    check_built(p, d, 2);
+    const Plan q = build_update_plan(d.data(), n, 3000, kUpdateSegmentCost);
+    EXPECT(q.chunk == 3000, "explicit update chunk became %lld", (long long)q.chunk);
+    check_built(q, d, 2);
 }
 
 // The arrival pass addresses each segment's vector body (16-byte vectors of
@@ -67,7 +92,7 @@ static void check_plan(const std::vector<somaopt_tensor_desc>& d, int pass, int6
 // largest norm-pass chunk a normaliser allows, every arrival segment must
 // still span fewer than 2^31 bytes.  Gradients may not overlap for arrival,
 // and arriving buffers sit in an arena of their own.
-static void check_arrival_offsets(const std::vector<somaopt_tensor_desc>& d, std::mt19937_64& rng) {
+static void check_arrival_offsets(const std::vector<somaopt_tensor_desc>& d, std::mt19937_64& rng, bool full) {
     std::vector<somaopt_tensor_desc> big = d;
     std::vector<const void*> inc(d.size(), nullptr);
     uintptr_t ga = 6ull << 40, ia = 7ull << 40;
@@ -87,6 +112,15 @@ static void check_arrival_offsets(const std::vector<somaopt_tensor_desc>& d, std
         EXPECT(g.numel <= chunk, "arrival segment of %lld elements", (long long)g.numel);
         EXPECT(16 * g.nvec < (int64_t(1) << 31), "arrival segment body of %lld bytes", (long long)(16 * g.nvec));
     }
+    if (!full) return;
+    // the arrival plan the library builds by default: the norm pass's chunk,
+    // at most kStreamingPass3Chunk when that plan streams
+    const Plan a = build_arrival_plan(big.data(), (int64_t)big.size(), kDefaultPass1Chunk, 0, inc.data());
+    const bool streams = streaming_plan(build_plan(big.data(), (int64_t)big.size(), 3, kDefaultPass1Chunk,
+                                                   kSegmentCost, inc.data()));
+    EXPECT(a.chunk == (streams ? kStreamingPass3Chunk : kDefaultPass1Chunk), "arrival plan chunk %lld",
+           (long long)a.chunk);
+    check_built(a, big, 3);
 }
 
 int main() {
@@ -127,7 +161,8 @@ int main() {
         const int64_t ch2 = normalise_chunk((int64_t)(rng() % 20000), kDefaultPass2Chunk);
         check_plan(d, 1, ch1);
         check_plan(d, 2, ch2);
-        check_arrival_offsets(d, rng);
+        check_update_plan(d);
+        check_arrival_offsets(d, rng, trial % 10 == 0);
         // a corrupted copy of the table must be rejected
         std::vector<somaopt_tensor_desc> bad = d;
         const int j = (int)(rng() % n);
