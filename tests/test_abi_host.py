@@ -358,3 +358,20 @@ def test_noalloc_init_refuses_tables_beyond_its_scratch():
     assert rc == S.E_INVALID and not h.value
     msg = S.last_error()
     assert "bytes of device scratch" in msg and "33554432" in msg, msg
+
+
+def test_bench_cpu_baseline_runs_the_oracle_on_the_host_pool():
+    """The bench's CPU baseline: the oracle's whole step (sum of squares, clip
+    coefficient, update of every element) timed on a pool of host threads; the
+    line reports the threads it used and what the sample was."""
+    import sys
+    sys.path.insert(0, ROOT)
+    import bench
+    from tensor_optimizer_step_amd import workloads as W
+    wl = W.tiny()
+    cores, model = bench.cpu_pool()
+    rec = bench.cpu_baseline_workload(wl, 0.2)
+    assert rec["kind"] == "oracle" and rec["unit"] == "param-elements/s"
+    assert rec["cores"] == cores >= 1 and rec["value"] > 0
+    assert f"first {wl.n_tensors} tensors of tiny ({wl.trainable_numel} elements)" in rec["sample"]
+    assert model in rec["sample"]
